@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the decode-step S2ANTA-prop path on one MI355X.
+
+One step = one santa_decode_prop call (pass 1, reducer, pass 2) over one
+decode step of the Llama-3.1-8B layer shape at 32k context: batch 1, 32 query
+heads, 8 KV heads, head dim 128, bf16 KV, S = 128, tiles of 256 tokens
+(synthetic inputs with planted high-scoring keys and 4 sinks per KV head).
+Inputs are resident in HBM before timing starts; steps rotate over enough
+copies of the KV cache (>= 1 GiB) that the 256 MB Infinity Cache cannot hold
+them.  The same GPU's exact split-KV decode is timed the same way, and the
+fp64 CPU oracle is timed on a bounded sample on the host.
+
+Prints one JSON line (see the "value"/"roofline"/"cpu_baseline" fields).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn µs/step + achieved HBM GB/s (% peak), 32k ctx, S=128, 1×MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+KERNEL_SOURCES = ["santa_kernels.hip", "santa_score.h", "santa_device.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "stochastic_sparse_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    e = t.get("kernels", {}).get(kernel_key)
+    return None if e is None else e.get("bytes_per_launch")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_steps(fn, steps, warmup, events=None):
+    """Run fn(i) warmup times untimed then `steps` times timed; returns
+    (ms_per_step, per-step dominant-kernel ms list or None)."""
+    import torch
+    import stochastic_sparse_attention_amd as sa
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    pairs = None
+    if events:
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(steps)]
+        for a, b in pairs:          # create the HIP events (torch creates them on first record)
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if pairs:
+            sa.santa_set_timing_events(pairs[i][0], pairs[i][1])
+        fn(warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sa.santa_set_timing_events(None, None)
+    kern = None
+    if pairs:
+        kern = [a.elapsed_time(b) for a, b in pairs]
+    return (t1 - t0) * 1e3 / steps, kern
+
+
+def cpu_baseline(inp, S, seconds):
+    """The fp64 oracle on the host cores (a reported baseline, not the target)."""
+    import oracle as O
+    prob = O.Problem.from_inputs(inp)
+    u = inp.u(S)
+    reps, secs = 0, []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        O.santa_prop(prob, inp.q, inp.k, inp.v, S, u)
+        secs.append(time.perf_counter() - t0)
+        reps += 1
+        if time.perf_counter() - t_start >= seconds or reps >= 50:
+            break
+    return float(np.median(secs)), reps, O.num_threads()
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload id (2 = 32k decode layer)")
+    ap.add_argument("--kv-bytes-min", type=float, default=1.0, help="GiB of rotated KV copies")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-exact", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        log("bench.py: only single-GPU runs are supported (the path is not sharded in this build)")
+        return 2
+
+    import torch
+    import stochastic_sparse_attention_amd as sa
+    from stochastic_sparse_attention_amd import bytemodel as BM
+    from stochastic_sparse_attention_amd import synth
+    from stochastic_sparse_attention_amd.device_io import to_device
+
+    sa._lib.load()
+    dev0 = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.config]
+    S, T = cfg.S, cfg.tile_len
+    log(f"bench: generating workload {cfg.cid} ({cfg.name})")
+    inp = synth.make_inputs(cfg, cfg.cid)
+    dev = to_device(inp, dev0)
+    kvb = BM.kv_bytes(cfg)
+    ncopy = max(1, int(np.ceil(args.kv_bytes_min * 2 ** 30 / (2 * kvb))))
+    ks = [dev.k] + [dev.k.clone() for _ in range(ncopy - 1)]
+    vs = [dev.v] + [dev.v.clone() for _ in range(ncopy - 1)]
+    BH = cfg.batch * cfg.num_q_heads
+    u = dev.u(S)
+    out = torch.empty((BH, cfg.head_dim), dtype=torch.float32, device=dev0)
+    ws = torch.empty(sa.santa_workspace_size(dev.problem, "prop", S), dtype=torch.uint8, device=dev0)
+    log(f"bench: {ncopy} KV copies ({ncopy * 2 * kvb / 2**30:.2f} GiB), S={S}, T={T}")
+
+    def prop_step(i):
+        c = i % ncopy
+        sa.santa_decode_prop(dev.problem, dev.q, ks[c], vs[c], S, u, out, workspace=ws)
+
+    ms, kern = time_steps(prop_step, args.steps, args.warmup, events=True)
+    log(f"bench: prop {ms * 1e3:.2f} us/step, pass-1 {np.mean(kern) * 1e3:.2f} us")
+
+    # one more call with the optional outputs, for the byte count and V-row share
+    max_nt = (cfg.seq_len + T - 1) // T
+    idx = torch.empty((BH, S), dtype=torch.int32, device=dev0)
+    tb = torch.empty((BH, max_nt), dtype=torch.int32, device=dev0)
+    sa.santa_decode_prop(dev.problem, dev.q, dev.k, dev.v, S, u, out, idx, tb, workspace=ws)
+    torch.cuda.synchronize()
+    tb_np, idx_np = tb.cpu().numpy(), idx.cpu().numpy()
+    seq = inp.seq_lens if not inp.uniform_len or cfg.page_size else None
+    nbytes = BM.prop_step_bytes(cfg, S, tb_np, T, seq)
+    pass1_bytes = nbytes["pass1"]
+    kern_ms = float(np.mean(kern))
+    achieved = pass1_bytes / (kern_ms * 1e-3) / 1e9
+    step_gbs = nbytes["total"] / (ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(step_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: S2ANTA-prop", "batch": cfg.batch,
+                   "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads,
+                   "head_dim": cfg.head_dim, "seq_len": cfg.seq_len, "S": S, "tile_len": T,
+                   "kv_copies_rotated": ncopy},
+        "us_per_step": round(ms * 1e3, 3),
+        "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
+        "algorithmic_bytes_per_step": nbytes,
+        "v_row_fraction": round(BM.v_row_fraction(idx_np, cfg, seq), 6),
+        "tiles_visited_per_head": round(float((tb_np > 0).sum(1).mean()), 2),
+        "roofline": {"kernel": "prop_pass1_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic("prop_pass1_kernel"),
+                     "bytes_per_launch": pass1_bytes, "avg_launch_us": round(kern_ms * 1e3, 3)},
+    }
+
+    if not args.no_exact:
+        wse = torch.empty(sa.santa_workspace_size(dev.problem, "exact"), dtype=torch.uint8, device=dev0)
+        oute = torch.empty_like(out)
+
+        def exact_step(i):
+            c = i % ncopy
+            sa.exact_decode_ref(dev.problem, dev.q, ks[c], vs[c], oute, workspace=wse)
+
+        ems, ekern = time_steps(exact_step, args.steps, args.warmup, events=True)
+        eb = BM.exact_step_bytes(cfg, T, seq)
+        log(f"bench: exact {ems * 1e3:.2f} us/step, partial {np.mean(ekern) * 1e3:.2f} us")
+        result["exact_decode_ref"] = {
+            "us_per_step": round(ems * 1e3, 3),
+            "GB/s": round(eb["total"] / (ems * 1e-3) / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * eb["total"] / (ems * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "partial_kernel_us": round(float(np.mean(ekern)) * 1e3, 3),
+            "partial_kernel_GB/s": round(eb["partial"] / (np.mean(ekern) * 1e-3) / 1e9, 1),
+        }
+        result["speedup_vs_exact"] = round(ems / ms, 3)
+
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle")
+        sec, reps, cores = cpu_baseline(inp, S, args.cpu_seconds)
+        result["cpu_baseline"] = {
+            "value": round(nbytes["total"] / sec / 1e9, 3), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "us_per_step": round(sec * 1e6, 1),
+            "sample": f"{reps} full steps of the same workload (all {BH} heads), median",
+        }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,170 @@
+/*
+ * santa.h -- C ABI of the decode-step stochastic sparse attention library
+ * (libsanta.so, gfx950 / MI355X).
+ *
+ * The method is SANTA as described on the web page "Stochastic Sparse
+ * Attention for Memory-Bound Inference" (ICML 2026 paper notes).  For each
+ * query head of one decode step the library scores the whole KV cache, forms
+ * the softmax distribution A, and instead of the full A.V product draws S
+ * indices from A by systematic sampling (one offset U in [0, 1/S), thresholds
+ * U + m/S, m = 0..S-1; "key design 1") and averages the S matching V rows.
+ * Two GPU schedules are offered: S2ANTA-prop ("key design 2": exact scores
+ * and a stash in pass 1, a global reducer that gives every tile a budget
+ * equal to the number of thresholds falling in its CDF interval, sampling
+ * and the V gather in pass 2) and S2ANTA-flash ("key design 3": every tile
+ * samples S/n_t tokens from its own softmax, partial means are rescaled by
+ * the true tile mass at merge time).  exact_decode_ref is the same GPU's
+ * exact split-KV decode, the baseline the pages compare against
+ * (FlashDecoding-style, "key design 2" and related work).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer unless its comment says host.
+ *   - The caller owns all memory.  The library allocates nothing, keeps no
+ *     global state except the optional timing hook below, and is reentrant.
+ *   - Work is launched asynchronously on `stream` (a hipStream_t; NULL is the
+ *     null stream).  Results are valid once the stream has synchronised.
+ *   - Arguments are validated on the host before anything is launched.  On
+ *     any error nothing is launched and no output is written.
+ *   - For identical inputs results are bitwise identical from run to run (no
+ *     floating-point atomics; every reduction has a fixed order).
+ *   - No C++ exception crosses this boundary.
+ *
+ * Layouts (row-major, last index fastest)
+ *   q     [B, Hq, d]                          q_dtype
+ *   k, v  contiguous: [B, Hkv, max_seq_len, d]   kv_dtype
+ *         paged:      [num_pages, Hkv, page_size, d]; token j of request b
+ *                     is row (j % page_size) of page page_table[b][j / page_size]
+ *   u     [B*Hq] fp32, u[b*Hq+h] in [0, 1/S)  (one offset per head; a caller
+ *         wanting one offset per request replicates it over the heads)
+ *   out   [B, Hq, d] fp32
+ *   q head h reads KV head h / (Hq / Hkv)     (grouped-query attention)
+ */
+#ifndef SANTA_H
+#define SANTA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+typedef enum {
+    SANTA_OK = 0,
+    SANTA_ERR_INVALID = -1,      /* null required pointer, bad size, bad combination */
+    SANTA_ERR_UNSUPPORTED = -2,  /* valid but not built: head_dim, dtype, group, tile */
+    SANTA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required        */
+    SANTA_ERR_HIP = -4           /* a HIP launch reported an error                    */
+} santa_status;
+
+typedef enum { SANTA_F32 = 0, SANTA_BF16 = 1 } santa_dtype;
+
+typedef enum {
+    SANTA_VARIANT_PROP = 0,
+    SANTA_VARIANT_FLASH = 1,
+    SANTA_VARIANT_EXACT = 2
+} santa_variant;
+
+/* Shapes and layout of one decode-attention call. */
+typedef struct {
+    int32_t batch;            /* B >= 0; B == 0 is a no-op that returns SANTA_OK   */
+    int32_t num_q_heads;      /* Hq >= 1                                           */
+    int32_t num_kv_heads;     /* Hkv >= 1, Hq % Hkv == 0, group Hq/Hkv in {1,2,4,8} */
+    int32_t head_dim;         /* d; only 128 is built                              */
+    int32_t max_seq_len;      /* n_k (contiguous) or the longest request (ragged)  */
+    const int32_t *seq_lens;  /* device [B] keys per request, or NULL: every
+                                 request has max_seq_len keys.  A value <= 0 makes
+                                 that request empty: its output rows are 0, its
+                                 sample indices -1 and its budgets 0.  Values
+                                 above max_seq_len are clamped to it.              */
+    int32_t q_dtype;          /* santa_dtype; must equal kv_dtype                  */
+    int32_t kv_dtype;         /* santa_dtype                                       */
+    int32_t page_size;        /* 0: contiguous K/V.  Else a multiple of 16 and a
+                                 divisor of tile_len: paged pools                  */
+    const int32_t *page_table;/* device [B, max_pages_per_seq] (paged only)        */
+    int32_t max_pages_per_seq;/* >= ceil(max_seq_len / page_size) (paged only)     */
+    float scale;              /* softmax scale, normally (float)(1/sqrt(d))        */
+    int32_t tile_len;         /* T, tokens per tile: multiple of 64, 64..1024      */
+} santa_problem;
+
+/*
+ * Bytes of device workspace the given variant needs for this problem and S
+ * (S is ignored for SANTA_VARIANT_EXACT).  Writes *bytes; returns a status
+ * (the same validation as the decode calls).  The workspace must be 256-byte
+ * aligned; its contents need not be initialised.
+ */
+int santa_workspace_size(const santa_problem *p, int32_t variant, int32_t S, size_t *bytes);
+
+/*
+ * S2ANTA-prop ("key design 2").  Pass 1 streams K once per tile of T tokens,
+ * computes the group's scores, the per-tile max and partition function and
+ * writes the exponentiated scores to a stash; a reducer per head forms the
+ * tile CDF and gives tile t a budget S_t equal to the number of thresholds
+ * U + m/S inside its CDF interval (so sum_t S_t = S and tiles of low mass
+ * get 0 and are never read again); pass 2 scans the stash of each tile with
+ * S_t > 0, inverts its CDF at its thresholds, gathers those V rows and
+ * divides the sum by S.  This equals untiled systematic sampling.
+ *
+ *   S            samples per head, 1 <= S <= 65536
+ *   u            [B*Hq] offsets in [0, 1/S) (not checked on the device)
+ *   out          [B, Hq, d] fp32 estimate
+ *   sample_idx   [B, Hq, S] int32 or NULL: token selected by threshold m,
+ *                in threshold order (repeats mean multiplicity)
+ *   tile_budget  [B, Hq, ceil(max_seq_len/T)] int32 or NULL: S_t per tile
+ *   workspace    santa_workspace_size(p, SANTA_VARIANT_PROP, S) bytes
+ */
+int santa_decode_prop(const santa_problem *p, const void *q, const void *k, const void *v,
+                      int32_t S, const float *u, float *out, int32_t *sample_idx,
+                      int32_t *tile_budget, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/*
+ * S2ANTA-flash ("key design 3").  No global step between scoring and
+ * sampling: each tile of T tokens takes S_f = S / n_t samples from its own
+ * softmax with thresholds u_f + m/S_f, u_f = U * n_t (one offset per head,
+ * scaled to the tile budget), and averages those V rows; the merge weighs
+ * every tile's mean by its true share of the mass.  Requires seq_lens ==
+ * NULL (every request has max_seq_len keys) and S % n_t == 0 with
+ * n_t = ceil(max_seq_len / T), else SANTA_ERR_INVALID.
+ *
+ *   sample_idx   [B, Hq, S] int32 or NULL, tile-major: tile t's samples are
+ *                entries t*S_f .. t*S_f + S_f - 1
+ *   tile_budget  ignored (every tile's budget is S_f); may be NULL
+ *   workspace    santa_workspace_size(p, SANTA_VARIANT_FLASH, S) bytes
+ */
+int santa_decode_flash(const santa_problem *p, const void *q, const void *k, const void *v,
+                       int32_t S, const float *u, float *out, int32_t *sample_idx,
+                       int32_t *tile_budget, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/*
+ * Exact split-KV decode on the same GPU: out = softmax(scale * q K^T) V per
+ * head, computed per tile (max, sum, weighted V sum) and merged.  This is
+ * the baseline that S2ANTA is measured against.
+ *   workspace    santa_workspace_size(p, SANTA_VARIANT_EXACT, 0) bytes
+ */
+int exact_decode_ref(const santa_problem *p, const void *q, const void *k, const void *v,
+                     float *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Optional timing hook for benchmarks.  When both events are non-NULL
+ * (hipEvent_t), every later decode call made from the calling thread
+ * records `begin` just before and `end` just after its dominant kernel (the
+ * one that streams K: pass 1 for prop, the tile kernel for flash, the
+ * partial kernel for exact) on the call's stream.  Pass NULL, NULL to turn
+ * it off.  Thread-local; returns SANTA_OK.
+ */
+int santa_set_timing_events(void *begin_event, void *end_event);
+
+/* Static description of a status code. */
+const char *santa_status_string(int status);
+
+/* Library ABI version (increments on any signature or layout change). */
+int santa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SANTA_H */

@@ -32,7 +32,8 @@
  *   R5  the tile length T is given in tokens; n_t = ceil(n_k / T);
  *   R6  flash uses one offset per head, scaled to the per-tile budget:
  *       u_f = U * n_t in [0, 1/S_f), S_f = S / n_t;
- *   R10 GQA maps q head h to KV head h / (Hq / Hkv).
+ *   R10 GQA maps q head h to KV head h / (Hq / Hkv);
+ *   R11 a request with zero keys is empty: output 0, indices -1, budgets 0.
  *
  * All arithmetic is IEEE double.  Inputs (bf16 or fp32) are widened exactly.
  */
@@ -217,6 +218,9 @@ static void mean_of_rows(const oracle_problem *p, const void *v, int b, int g,
     for (int i = 0; i < d; ++i) out[i] /= (double)count;
 }
 
+/* Reading R11 (empty requests): a request with no keys has no distribution
+   to sample from; its output rows are 0, it selects no token (index -1) and
+   every tile budget is 0.  Lengths must lie in [0, max_seq_len]. */
 static int lengths_ok(const oracle_problem *p)
 {
     if (p->batch <= 0 || p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->head_dim <= 0 ||
@@ -224,7 +228,7 @@ static int lengths_ok(const oracle_problem *p)
         return 0;
     for (int b = 0; b < p->batch; ++b) {
         int n = seq_len_of(p, b);
-        if (n <= 0 || n > p->max_seq_len) return 0;
+        if (n < 0 || n > p->max_seq_len) return 0;
     }
     return 1;
 }
@@ -266,6 +270,16 @@ int oracle_santa_prop(const oracle_problem *p, const void *q, const void *k,
 #pragma omp parallel for schedule(dynamic, 1)
     for (int bh = 0; bh < nheads; ++bh) {
         int b = bh / H, h = bh % H, g = kv_head_of(p, h), n = seq_len_of(p, b);
+        if (n == 0) {                                   /* R11 */
+            for (int i = 0; i < d; ++i) out[(size_t)bh * d + i] = 0.0;
+            for (int m = 0; m < S; ++m) {
+                if (idx) idx[(size_t)bh * S + m] = -1;
+                if (delta) delta[(size_t)bh * S + m] = INFINITY;
+            }
+            if (tile_cnt)
+                for (int i = 0; i < mnt; ++i) tile_cnt[(size_t)bh * mnt + i] = 0;
+            continue;
+        }
         double *x = (double *)malloc(sizeof(double) * (size_t)n);
         double *e = (double *)malloc(sizeof(double) * (size_t)n);
         double *t = (double *)malloc(sizeof(double) * (size_t)S);
@@ -375,12 +389,13 @@ int oracle_exact(const oracle_problem *p, const void *q, const void *k,
 #pragma omp parallel for schedule(dynamic, 1)
     for (int bh = 0; bh < nheads; ++bh) {
         int b = bh / H, h = bh % H, g = kv_head_of(p, h), n = seq_len_of(p, b);
+        double *o = out + (size_t)bh * d;
+        for (int i = 0; i < d; ++i) o[i] = 0.0;
+        if (n == 0) continue;                           /* R11 */
         double *x = (double *)malloc(sizeof(double) * (size_t)n);
         double *e = (double *)malloc(sizeof(double) * (size_t)n);
         oracle_logits(p, q, k, b, h, x);
         double Z = oracle_softmax_weights(x, n, e, NULL);
-        double *o = out + (size_t)bh * d;
-        for (int i = 0; i < d; ++i) o[i] = 0.0;
         for (int j = 0; j < n; ++j) {
             double a = e[j] / Z;
             size_t off = kv_row_offset(p, b, g, j);
@@ -409,9 +424,19 @@ int oracle_replay(const oracle_problem *p, const void *v, int S, const int *idx,
         int b = bh / H, h = bh % H, g = kv_head_of(p, h), n = seq_len_of(p, b);
         const int *I = idx + (size_t)bh * S;
         int bad = 0;
+        double *o = out + (size_t)bh * d;
+        if (n == 0) {                                   /* R11 */
+            for (int m = 0; m < S; ++m)
+                if (I[m] != -1) bad = 1;
+            for (int i = 0; i < d; ++i) o[i] = 0.0;
+            if (bad) {
+#pragma omp atomic write
+                status = -2;
+            }
+            continue;
+        }
         for (int m = 0; m < S; ++m)
             if (I[m] < 0 || I[m] >= n) bad = 1;
-        double *o = out + (size_t)bh * d;
         if (bad) {
 #pragma omp atomic write
             status = -2;

@@ -1,0 +1,82 @@
+"""ctypes binding of libsanta.so (the C ABI declared in include/santa.h).
+
+Argument marshalling only: tensors are passed as raw device pointers and the
+current torch stream as the hipStream_t; every step of the computation runs
+in the library's HIP kernels.  There is no fallback: if the library has not
+been built, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsanta.so")
+
+SANTA_OK, SANTA_ERR_INVALID, SANTA_ERR_UNSUPPORTED, SANTA_ERR_WORKSPACE, SANTA_ERR_HIP = 0, -1, -2, -3, -4
+SANTA_F32, SANTA_BF16 = 0, 1
+VARIANT = {"prop": 0, "flash": 1, "exact": 2}
+
+EXPORTS = [
+    "santa_workspace_size", "santa_decode_prop", "santa_decode_flash", "exact_decode_ref",
+    "santa_set_timing_events", "santa_status_string", "santa_abi_version",
+]
+
+
+class SantaError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: status {status} ({msg})")
+        self.status = status
+
+
+class santa_problem(C.Structure):
+    _fields_ = [
+        ("batch", C.c_int32), ("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
+        ("head_dim", C.c_int32), ("max_seq_len", C.c_int32),
+        ("seq_lens", C.c_void_p),
+        ("q_dtype", C.c_int32), ("kv_dtype", C.c_int32),
+        ("page_size", C.c_int32), ("page_table", C.c_void_p),
+        ("max_pages_per_seq", C.c_int32), ("scale", C.c_float), ("tile_len", C.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load():
+    """Load libsanta.so; raises if it is missing (no fallback path exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m stochastic_sparse_attention_amd.build` "
+            "(or __graft_entry__.build()) first")
+    L = C.CDLL(LIB_PATH)
+    P = C.POINTER(santa_problem)
+    vp, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+    L.santa_workspace_size.argtypes = [P, i32, i32, C.POINTER(sz)]
+    L.santa_workspace_size.restype = C.c_int
+    sampled = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.santa_decode_prop.argtypes = sampled
+    L.santa_decode_prop.restype = C.c_int
+    L.santa_decode_flash.argtypes = sampled
+    L.santa_decode_flash.restype = C.c_int
+    L.exact_decode_ref.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+    L.exact_decode_ref.restype = C.c_int
+    L.santa_set_timing_events.argtypes = [vp, vp]
+    L.santa_set_timing_events.restype = C.c_int
+    L.santa_status_string.argtypes = [C.c_int]
+    L.santa_status_string.restype = C.c_char_p
+    L.santa_abi_version.restype = C.c_int
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return load().santa_status_string(status).decode()
+
+
+def _check(fn, status):
+    if status != SANTA_OK:
+        raise SantaError(fn, status, status_string(status))

@@ -1,0 +1,228 @@
+// santa_api.cpp -- the C ABI of libsanta: host-side validation, workspace
+// sizing and carving, and launch sequencing.  See include/santa.h for the
+// contract of every entry point.
+#include "../../include/santa.h"
+
+#include <hip/hip_runtime.h>
+
+#include "santa_launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kHeadDimBuilt = 128;
+constexpr int kMaxTiles = 4096;       // merge keeps one fp64 weight per tile in LDS
+constexpr int kMaxSamples = 65536;
+
+thread_local void *g_ev_begin = nullptr;
+thread_local void *g_ev_end = nullptr;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Derived {
+    int group = 0;
+    int max_nt = 0;
+    int kmax = 0;
+    int nwg = 0;
+};
+
+bool tile_len_built(int T) { return T == 64 || T == 128 || T == 256 || T == 512 || T == 1024; }
+
+// Shape/layout checks shared by every variant.  S is checked for prop/flash.
+int validate(const santa_problem *p, int variant, int S, Derived *d) {
+    if (!p) return SANTA_ERR_INVALID;
+    if (variant < SANTA_VARIANT_PROP || variant > SANTA_VARIANT_EXACT) return SANTA_ERR_INVALID;
+    if (p->batch < 0 || p->num_q_heads < 1 || p->num_kv_heads < 1 || p->head_dim < 1 ||
+        p->max_seq_len < 1 || p->tile_len < 1)
+        return SANTA_ERR_INVALID;
+    if (p->num_q_heads % p->num_kv_heads) return SANTA_ERR_INVALID;
+    if (p->tile_len % 64) return SANTA_ERR_INVALID;
+    if (p->q_dtype != SANTA_F32 && p->q_dtype != SANTA_BF16) return SANTA_ERR_INVALID;
+    if (p->kv_dtype != SANTA_F32 && p->kv_dtype != SANTA_BF16) return SANTA_ERR_INVALID;
+    if (!(p->scale > 0.0f) || p->scale != p->scale) return SANTA_ERR_INVALID;
+    if (p->page_size < 0) return SANTA_ERR_INVALID;
+    if (p->page_size > 0) {
+        if (p->page_size % 16) return SANTA_ERR_INVALID;
+        if (!p->page_table) return SANTA_ERR_INVALID;
+        const long need = ((long)p->max_seq_len + p->page_size - 1) / p->page_size;
+        if (p->max_pages_per_seq < need) return SANTA_ERR_INVALID;
+    }
+    const int G = p->num_q_heads / p->num_kv_heads;
+    if (p->head_dim != kHeadDimBuilt) return SANTA_ERR_UNSUPPORTED;
+    if (p->q_dtype != p->kv_dtype) return SANTA_ERR_UNSUPPORTED;
+    if (!(G == 1 || G == 2 || G == 4 || G == 8)) return SANTA_ERR_UNSUPPORTED;
+    if (!tile_len_built(p->tile_len)) return SANTA_ERR_UNSUPPORTED;
+    const long nt = ((long)p->max_seq_len + p->tile_len - 1) / p->tile_len;
+    if (nt > kMaxTiles) return SANTA_ERR_UNSUPPORTED;
+    if ((long)p->batch * p->num_kv_heads * nt > 0x7fffffffL) return SANTA_ERR_UNSUPPORTED;
+    if ((long)p->batch * p->num_q_heads * 8 > 0x7fffffffL) return SANTA_ERR_UNSUPPORTED;
+    if (variant != SANTA_VARIANT_EXACT) {
+        if (S < 1 || S > kMaxSamples) return SANTA_ERR_INVALID;
+    }
+    if (variant == SANTA_VARIANT_FLASH) {
+        if (p->seq_lens) return SANTA_ERR_INVALID;
+        if (S % nt) return SANTA_ERR_INVALID;
+    }
+    d->group = G;
+    d->max_nt = (int)nt;
+    d->kmax = (variant == SANTA_VARIANT_PROP) ? (S < nt ? S : (int)nt) : 0;
+    int nwg = (d->kmax + 7) / 8;
+    d->nwg = nwg < 1 ? 1 : (nwg > 8 ? 8 : nwg);
+    return SANTA_OK;
+}
+
+// Workspace layout (each region 256-byte aligned).  With base == nullptr it
+// only sizes.
+size_t carve(const santa_problem *p, int variant, const Derived &d, char *base, santa::Workspace *ws) {
+    const size_t BH = (size_t)p->batch * p->num_q_heads;
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> void * {
+        void *ptr = base ? base + off : nullptr;
+        off += align_up(bytes);
+        return ptr;
+    };
+    santa::Workspace w{};
+    if (variant == SANTA_VARIANT_PROP) {
+        w.stash = take(BH * (size_t)p->max_seq_len * sizeof(float));
+        w.stats = take(BH * (size_t)d.max_nt * 2 * sizeof(float));
+        w.vis = take(BH * (size_t)d.kmax * santa::visit_record_bytes());
+        w.vis_count = take(BH * sizeof(int));
+        w.counters = take(BH * sizeof(int));
+        w.part = take(BH * (size_t)(4 * d.nwg) * kHeadDimBuilt * sizeof(float));
+    } else {
+        w.part_m = take(BH * (size_t)d.max_nt * sizeof(float));
+        w.part_l = take(BH * (size_t)d.max_nt * sizeof(float));
+        w.part_o = take(BH * (size_t)d.max_nt * kHeadDimBuilt * sizeof(float));
+    }
+    if (ws) *ws = w;
+    return off;
+}
+
+int check_workspace(const santa_problem *p, int variant, const Derived &d, void *workspace,
+                    size_t workspace_bytes, santa::Workspace *ws) {
+    const size_t need = carve(p, variant, d, nullptr, nullptr);
+    if (!workspace || workspace_bytes < need) return SANTA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace) % kAlign) return SANTA_ERR_WORKSPACE;
+    carve(p, variant, d, (char *)workspace, ws);
+    return SANTA_OK;
+}
+
+santa::LaunchArgs make_args(const santa_problem *p, const Derived &d, const void *q, const void *k,
+                            const void *v, int S, const float *u, float *out, int *sample_idx,
+                            int *tile_budget, const santa::Workspace &ws, void *stream) {
+    santa::LaunchArgs a{};
+    a.batch = p->batch;
+    a.num_q_heads = p->num_q_heads;
+    a.num_kv_heads = p->num_kv_heads;
+    a.group = d.group;
+    a.max_seq_len = p->max_seq_len;
+    a.max_nt = d.max_nt;
+    a.tile_len = p->tile_len;
+    a.seq_lens = p->seq_lens;
+    a.page_size = p->page_size;
+    a.page_table = p->page_table;
+    a.max_pages = p->max_pages_per_seq;
+    a.bf16 = p->kv_dtype == SANTA_BF16;
+    a.scale = p->scale;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.S = S;
+    a.u = u;
+    a.out = out;
+    a.sample_idx = sample_idx;
+    a.tile_budget = tile_budget;
+    a.kmax = d.kmax;
+    a.nwg = d.nwg;
+    a.ws = ws;
+    a.stream = stream;
+    return a;
+}
+
+int run_sampled(int variant, const santa_problem *p, const void *q, const void *k, const void *v,
+                int32_t S, const float *u, float *out, int32_t *sample_idx, int32_t *tile_budget,
+                void *workspace, size_t workspace_bytes, void *stream) {
+    Derived d;
+    int st = validate(p, variant, S, &d);
+    if (st != SANTA_OK) return st;
+    if (p->batch == 0) return SANTA_OK;
+    if (!q || !k || !v || !u || !out) return SANTA_ERR_INVALID;
+    santa::Workspace ws;
+    st = check_workspace(p, variant, d, workspace, workspace_bytes, &ws);
+    if (st != SANTA_OK) return st;
+    const santa::LaunchArgs a =
+        make_args(p, d, q, k, v, S, u, out, sample_idx,
+                  variant == SANTA_VARIANT_PROP ? tile_budget : nullptr, ws, stream);
+    const santa::TimingHook hook{g_ev_begin, g_ev_end};
+    const hipError_t e = variant == SANTA_VARIANT_PROP ? santa::launch_prop(a, hook)
+                                                       : santa::launch_flash(a, hook);
+    return e == hipSuccess ? SANTA_OK : SANTA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int santa_workspace_size(const santa_problem *p, int32_t variant, int32_t S, size_t *bytes) {
+    if (!bytes) return SANTA_ERR_INVALID;
+    Derived d;
+    const int st = validate(p, variant, variant == SANTA_VARIANT_EXACT ? 1 : S, &d);
+    if (st != SANTA_OK) return st;
+    *bytes = carve(p, variant, d, nullptr, nullptr);
+    return SANTA_OK;
+}
+
+int santa_decode_prop(const santa_problem *p, const void *q, const void *k, const void *v, int32_t S,
+                      const float *u, float *out, int32_t *sample_idx, int32_t *tile_budget,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    return run_sampled(SANTA_VARIANT_PROP, p, q, k, v, S, u, out, sample_idx, tile_budget, workspace,
+                       workspace_bytes, stream);
+}
+
+int santa_decode_flash(const santa_problem *p, const void *q, const void *k, const void *v, int32_t S,
+                       const float *u, float *out, int32_t *sample_idx, int32_t *tile_budget,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    return run_sampled(SANTA_VARIANT_FLASH, p, q, k, v, S, u, out, sample_idx, tile_budget, workspace,
+                       workspace_bytes, stream);
+}
+
+int exact_decode_ref(const santa_problem *p, const void *q, const void *k, const void *v, float *out,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+    Derived d;
+    int st = validate(p, SANTA_VARIANT_EXACT, 1, &d);
+    if (st != SANTA_OK) return st;
+    if (p->batch == 0) return SANTA_OK;
+    if (!q || !k || !v || !out) return SANTA_ERR_INVALID;
+    santa::Workspace ws;
+    st = check_workspace(p, SANTA_VARIANT_EXACT, d, workspace, workspace_bytes, &ws);
+    if (st != SANTA_OK) return st;
+    const santa::LaunchArgs a = make_args(p, d, q, k, v, 0, nullptr, out, nullptr, nullptr, ws, stream);
+    const santa::TimingHook hook{g_ev_begin, g_ev_end};
+    return santa::launch_exact(a, hook) == hipSuccess ? SANTA_OK : SANTA_ERR_HIP;
+}
+
+int santa_set_timing_events(void *begin_event, void *end_event) {
+    if (begin_event && end_event) {
+        g_ev_begin = begin_event;
+        g_ev_end = end_event;
+    } else {
+        g_ev_begin = nullptr;
+        g_ev_end = nullptr;
+    }
+    return SANTA_OK;
+}
+
+const char *santa_status_string(int status) {
+    switch (status) {
+        case SANTA_OK: return "ok";
+        case SANTA_ERR_INVALID: return "invalid argument";
+        case SANTA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case SANTA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case SANTA_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+int santa_abi_version(void) { return 1; }
+
+}  // extern "C"

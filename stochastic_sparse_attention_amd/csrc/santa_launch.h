@@ -1,0 +1,55 @@
+// santa_launch.h -- host-side interface between the C ABI (santa_api.cpp)
+// and the kernel launchers (santa_kernels.hip).  Internal to libsanta.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace santa {
+
+// Carved workspace regions (device pointers; unused ones are null).
+struct Workspace {
+    void *stash;      // prop: [B, Hq, max_seq_len] fp32
+    void *stats;      // prop: [B, Hq, max_nt] float2
+    void *vis;        // prop: [B, Hq, kmax] visit records
+    void *vis_count;  // prop: [B, Hq] int32
+    void *counters;   // prop: [B, Hq] int32 pass-2 arrival tickets
+    void *part;       // prop: [B, Hq, 4*nwg, d] fp32 wave partial sums
+    void *part_m;     // flash/exact: [B, Hq, max_nt] fp32
+    void *part_l;     // flash/exact: [B, Hq, max_nt] fp32
+    void *part_o;     // flash/exact: [B, Hq, max_nt, d] fp32
+};
+
+struct LaunchArgs {
+    int batch, num_q_heads, num_kv_heads, group;
+    int max_seq_len, max_nt, tile_len;
+    const int *seq_lens;
+    int page_size;
+    const int *page_table;
+    int max_pages;
+    int bf16;
+    float scale;
+    const void *q, *k, *v;
+    int S;
+    const float *u;
+    float *out;
+    int *sample_idx;
+    int *tile_budget;
+    int kmax;   // prop: visit-list capacity per head
+    int nwg;    // prop: pass-2 workgroups per head
+    Workspace ws;
+    void *stream;
+};
+
+struct TimingHook {
+    void *begin;
+    void *end;
+};
+
+hipError_t launch_prop(const LaunchArgs &a, const TimingHook &hook);
+hipError_t launch_flash(const LaunchArgs &a, const TimingHook &hook);
+hipError_t launch_exact(const LaunchArgs &a, const TimingHook &hook);
+size_t visit_record_bytes();
+
+}  // namespace santa

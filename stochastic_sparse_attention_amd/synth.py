@@ -92,16 +92,25 @@ CONFIGS = {
 # --------------------------------------------------------------------------
 # bf16 storage helpers (IEEE binary32 with the low 16 bits rounded away)
 # --------------------------------------------------------------------------
-def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round fp32 to bf16 (round to nearest, ties to even); return uint16 bits."""
+def f32_to_bf16_bits(x: np.ndarray, chunk: int = 1 << 24) -> np.ndarray:
+    """Round fp32 to bf16 (round to nearest, ties to even); return uint16 bits.
+
+    Works in uint32 on chunks (finite values cannot overflow: the largest
+    finite magnitude plus the rounding bias stays below 2^32); NaN maps to
+    the canonical quiet NaN.
+    """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
-    nan = np.isnan(x)
-    if nan.any():
-        r[nan] = 0x7FC0
-    return r
+    flat = x.reshape(-1).view(np.uint32)
+    out = np.empty(flat.size, np.uint16)
+    for s in range(0, flat.size, chunk):
+        u = flat[s:s + chunk]
+        lsb = (u >> 16) & np.uint32(1)
+        r = ((u + np.uint32(0x7FFF) + lsb) >> 16).astype(np.uint16)
+        nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+        if nan.any():
+            r[nan] = 0x7FC0
+        out[s:s + chunk] = r
+    return out.reshape(x.shape)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -206,7 +215,8 @@ def make_inputs(cfg: Config, seed: int) -> Inputs:
     if P:
         # logical page (b, i) -> physical page perm[offset_b + i]
         perm = rng.permutation(num_pages).astype(np.int32)
-        max_pages = int(pages_per.max())
+        # one row per request, wide enough for the longest allowed request
+        max_pages = (cfg.seq_len + P - 1) // P
         page_table = np.zeros((B, max_pages), np.int32)
         offs = np.concatenate([[0], np.cumsum(pages_per)])
         for b in range(B):

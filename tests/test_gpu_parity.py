@@ -1,0 +1,179 @@
+"""GPU parity: libsanta (through its C ABI) against the fp64 CPU oracle on the
+same seeded inputs and the same U.  See tests/parity.py for the bar."""
+import sys
+
+import numpy as np
+import pytest
+
+from stochastic_sparse_attention_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "gpu-marked tests need a GPU"
+    import stochastic_sparse_attention_amd._lib as L
+    L.load()                      # raises if libsanta.so is missing: no fallback
+    return torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(cfg, seed, gpu, **kw):
+    from stochastic_sparse_attention_amd.device_io import to_device
+    inp = synth.make_inputs(cfg, seed)
+    return to_device(inp, gpu, **kw)
+
+
+# ----------------------------------------------------------- prop, small
+def test_prop_cfg1_many_seeds(gpu):
+    """Single fp32 head, n_k=1024, S=16, T=128: 100 seeds, zero hard mismatches."""
+    import parity
+    tot = {"thresholds": 0, "mismatch": 0, "hard": 0, "exempt": 0}
+    for seed in list(range(1, 11)) + list(range(1000, 1090)):
+        rep = parity.check_prop(_dev(synth.CONFIGS[1], seed, gpu), 16, repeat=seed < 4)
+        for k in tot:
+            tot[k] += rep[k]
+    _say("cfg1 x100 seeds", tot)
+    assert tot["hard"] == 0
+
+
+@pytest.mark.parametrize("T", [64, 128, 256, 512, 1024])
+def test_prop_tiles_ragged_tail(gpu, T):
+    import parity
+    cfg = synth.small_config(2, batch=2, seq_len=4000)
+    rep = parity.check_prop(_dev(cfg, 3, gpu, tile_len=T), 128)
+    _say("T", T, rep)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (32, 8), (16, 2)])
+def test_prop_gqa_groups(gpu, hq, hkv):
+    import parity
+    cfg = synth.small_config(2, batch=1, seq_len=3000, num_q_heads=hq, num_kv_heads=hkv)
+    rep = parity.check_prop(_dev(cfg, 4, gpu), 64)
+    _say("G", hq // hkv, rep)
+
+
+@pytest.mark.parametrize("S", [1, 3, 128, 1000, 4096])
+def test_prop_budgets(gpu, S):
+    """S = 1, non-powers of two, and S far above the number of tiles (multiplicity)."""
+    import parity
+    cfg = synth.small_config(2, batch=1, seq_len=2500, num_q_heads=8, num_kv_heads=2)
+    rep = parity.check_prop(_dev(cfg, 5, gpu), S)
+    _say("S", S, rep)
+
+
+def test_prop_tiny_sequences(gpu):
+    """n_k = 1 and n_k shorter than one tile."""
+    import parity
+    for n in (1, 2, 63, 65, 255):
+        cfg = synth.small_config(2, batch=1, seq_len=n, hot=0, sinks=min(4, n), num_q_heads=8,
+                                 num_kv_heads=2)
+        rep = parity.check_prop(_dev(cfg, 6, gpu), 16)
+        _say("n", n, rep)
+
+
+def test_prop_one_hot_gives_exact_row(gpu):
+    """A logit gap of hundreds makes A one-hot: the output is exactly that V row."""
+    import parity
+    from stochastic_sparse_attention_amd.device_io import to_device
+    cfg = synth.small_config(2, batch=1, seq_len=2048, hot=0, sinks=0)
+    inp = synth.make_inputs(cfg, 7)
+    G = cfg.group
+    kv = inp.values("k").copy()
+    qv = inp.values("q")
+    kv *= 0.0
+    for g in range(cfg.num_kv_heads):
+        kv[0, g, 100 + 200 * g] = np.sign(qv[0, g * G:(g + 1) * G].mean(0)) * 1024.0
+    inp.k = synth.f32_to_bf16_bits(kv)
+    dev = to_device(inp, gpu)
+    out, idx, tb = parity.run_prop(dev, 128)
+    vv = inp.values("v")
+    for h in range(cfg.num_q_heads):
+        g = h // G
+        assert np.all(idx[h] == 100 + 200 * g)
+        assert np.array_equal(out[h], vv[0, g, 100 + 200 * g])
+    parity.check_prop(dev, 128)
+
+
+def test_prop_uniform_S_equals_nk_is_mean(gpu):
+    """Identical keys give a uniform A; with S = n_k every token is taken once."""
+    import parity
+    from stochastic_sparse_attention_amd.device_io import to_device
+    cfg = synth.small_config(2, batch=1, seq_len=1024, hot=0, sinks=0, num_q_heads=4, num_kv_heads=1)
+    inp = synth.make_inputs(cfg, 8)
+    inp.k[...] = inp.k[:, :, :1, :]
+    dev = to_device(inp, gpu)
+    out, idx, tb = parity.run_prop(dev, 1024)
+    for h in range(4):
+        assert np.array_equal(np.sort(idx[h]), np.arange(1024))
+    np.testing.assert_allclose(out, np.broadcast_to(inp.values("v")[0, 0].mean(0), out.shape), atol=1e-5)
+
+
+def test_prop_empty_and_ragged_requests(gpu):
+    import parity
+    cfg = synth.small_config(5, batch=5, seq_len=3000, min_seq_len=100)
+    inp = synth.make_inputs(cfg, 9)
+    seq = inp.seq_lens.copy()
+    seq[2] = 0
+    from stochastic_sparse_attention_amd.device_io import to_device
+    dev = to_device(inp, gpu, seq_lens=seq)
+    rep = parity.check_prop(dev, 128)
+    _say("empty+ragged", rep)
+
+
+def test_prop_paged_small(gpu):
+    import parity
+    cfg = synth.small_config(5, batch=6, seq_len=5000, min_seq_len=500)
+    rep = parity.check_prop(_dev(cfg, 10, gpu), 128)
+    _say("paged small", rep)
+
+
+# ------------------------------------------------------ flash and exact
+@pytest.mark.parametrize("T,S", [(256, 256), (256, 2048), (128, 64), (1024, 4)])
+def test_flash_small(gpu, T, S):
+    import parity
+    cfg = synth.small_config(3, batch=2, seq_len=4096)
+    rep = parity.check_flash(_dev(cfg, 11, gpu, tile_len=T), S)
+    _say("flash", T, S, rep)
+
+
+def test_flash_ragged_last_tile(gpu):
+    import parity
+    cfg = synth.small_config(3, batch=1, seq_len=1000)      # 4 tiles, last has 232 rows
+    rep = parity.check_flash(_dev(cfg, 12, gpu), 64)
+    _say("flash ragged", rep)
+
+
+def test_flash_fp32(gpu):
+    import parity
+    rep = parity.check_flash(_dev(synth.CONFIGS[1], 13, gpu), 64)
+    _say("flash fp32", rep)
+
+
+@pytest.mark.parametrize("cid,kw", [(1, {}), (2, dict(batch=2, seq_len=3000)),
+                                    (5, dict(batch=4, seq_len=4000, min_seq_len=300))])
+def test_exact_small(gpu, cid, kw):
+    import parity
+    rep = parity.check_exact(_dev(synth.small_config(cid, **kw), 14, gpu))
+    _say("exact", cid, rep)
+
+
+# ------------------------------------------------- full-size workloads
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_full_size_prop(gpu, cid):
+    import parity
+    cfg = synth.CONFIGS[cid]
+    _say("generating cfg", cid)
+    dev = _dev(cfg, cid, gpu)
+    rep = parity.check_prop(dev, cfg.S, repeat=cid == 2)
+    _say("full prop cfg", cid, rep)
+    if "exact" in cfg.variants:
+        _say("full exact cfg", cid, parity.check_exact(dev, repeat=False))
+    if "flash" in cfg.variants:
+        _say("full flash cfg", cid, parity.check_flash(dev, cfg.S_flash, repeat=False))

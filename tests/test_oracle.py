@@ -417,3 +417,36 @@ def test_prop_rejects_out_of_range_U():
     inp, prob = _small_inputs(1)
     with pytest.raises(ValueError):
         O.santa_prop(prob, inp.q, inp.k, inp.v, 16, np.array([1.0 / 16], np.float32))
+
+
+def test_empty_request_reading():
+    """R11: a request with no keys gives a zero output and selects nothing."""
+    cfg = synth.small_config(5, batch=3, seq_len=600, min_seq_len=100)
+    inp = synth.make_inputs(cfg, 2)
+    seq = inp.seq_lens.copy()
+    seq[1] = 0
+    prob = O.Problem(cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.seq_len,
+                     q_bf16=True, kv_bf16=True, scale=inp.scale, tile_len=cfg.tile_len,
+                     seq_lens=seq, page_size=cfg.page_size, page_table=inp.page_table)
+    S = cfg.S
+    r = O.santa_prop(prob, inp.q, inp.k, inp.v, S, inp.u(S))
+    H = cfg.num_q_heads
+    assert np.all(r["out"][H:2 * H] == 0) and np.all(r["idx"][H:2 * H] == -1)
+    assert np.all(r["tile_counts"][H:2 * H] == 0)
+    assert np.all(r["tile_counts"][:H].sum(1) == S)
+    ex = O.exact(prob, inp.q, inp.k, inp.v)
+    assert np.all(ex[H:2 * H] == 0)
+    np.testing.assert_array_equal(O.replay(prob, inp.v, S, r["idx"]), r["out"])
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10,
+                        np.array([0.0, -0.0, 1.0, 3.4e38, -3.4e38, 1e-40, np.inf, -np.inf], np.float32),
+                        # exact ties: low half 0x8000 with even and odd upper halves
+                        np.array([0x3F808000, 0x3F818000], np.uint32).view(np.float32)])
+    ours = synth.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    nan = synth.f32_to_bf16_bits(np.array([np.nan], np.float32))
+    assert np.isnan(synth.bf16_bits_to_f32(nan))[0]
