@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attn µs/step + achieved HBM GB/s (% peak), 32k ctx, S=128, 1×MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-KERNEL_SOURCES = ["santa_kernels.hip", "santa_score.h", "santa_device.h"]
+KERNEL_SOURCES = ["santa_prop.hip", "santa_flash.hip", "santa_exact.hip", "santa_kernels.h", "santa_score.h", "santa_device.h"]
 
 
 def kernel_source_hash():
@@ -89,6 +89,35 @@ def time_steps(fn, steps, warmup, events=None):
     return (t1 - t0) * 1e3 / steps, kern
 
 
+def time_graph(step_fn, ncopy, steps, warmup):
+    """Capture `ncopy` consecutive steps (one per KV copy) into one HIP graph
+    and replay it; returns ms per step.  Timed replays cover exactly `steps`
+    steps (rounded up to whole graphs)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(ncopy):          # warm the allocator / code paths on the side stream
+            step_fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(ncopy):
+            step_fn(i)
+    torch.cuda.synchronize()
+    for _ in range(max(1, warmup // ncopy)):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, -(-steps // ncopy))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / (reps * ncopy), g
+
+
 def cpu_baseline(inp, S, seconds):
     """The fp64 oracle on the host cores (a reported baseline, not the target)."""
     import oracle as O
@@ -116,6 +145,9 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-exact", action="store_true")
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
+                    help="graph: steps replayed from a captured HIP graph (value); "
+                         "eager: one host call per step")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -151,8 +183,12 @@ def main(argv=None):
         c = i % ncopy
         sa.santa_decode_prop(dev.problem, dev.q, ks[c], vs[c], S, u, out, workspace=ws)
 
-    ms, kern = time_steps(prop_step, args.steps, args.warmup, events=True)
-    log(f"bench: prop {ms * 1e3:.2f} us/step, pass-1 {np.mean(kern) * 1e3:.2f} us")
+    ms_eager, kern = time_steps(prop_step, args.steps, args.warmup, events=True)
+    log(f"bench: prop eager {ms_eager * 1e3:.2f} us/step, pass-1 {np.mean(kern) * 1e3:.2f} us")
+    ms = ms_eager
+    if args.mode == "graph":
+        ms, _g = time_graph(prop_step, ncopy, args.steps, args.warmup)
+        log(f"bench: prop graph {ms * 1e3:.2f} us/step")
 
     # one more call with the optional outputs, for the byte count and V-row share
     max_nt = (cfg.seq_len + T - 1) // T
@@ -186,6 +222,8 @@ def main(argv=None):
                    "head_dim": cfg.head_dim, "seq_len": cfg.seq_len, "S": S, "tile_len": T,
                    "kv_copies_rotated": ncopy},
         "us_per_step": round(ms * 1e3, 3),
+        "timing_mode": args.mode,
+        "eager_us_per_step": round(ms_eager * 1e3, 3),
         "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
         "algorithmic_bytes_per_step": nbytes,
         "v_row_fraction": round(BM.v_row_fraction(idx_np, cfg, seq), 6),
@@ -204,11 +242,16 @@ def main(argv=None):
             c = i % ncopy
             sa.exact_decode_ref(dev.problem, dev.q, ks[c], vs[c], oute, workspace=wse)
 
-        ems, ekern = time_steps(exact_step, args.steps, args.warmup, events=True)
+        ems_eager, ekern = time_steps(exact_step, args.steps, args.warmup, events=True)
+        ems = ems_eager
+        if args.mode == "graph":
+            ems, _ge = time_graph(exact_step, ncopy, args.steps, args.warmup)
         eb = BM.exact_step_bytes(cfg, T, seq)
-        log(f"bench: exact {ems * 1e3:.2f} us/step, partial {np.mean(ekern) * 1e3:.2f} us")
+        log(f"bench: exact {ems * 1e3:.2f} us/step (eager {ems_eager * 1e3:.2f}), "
+            f"partial {np.mean(ekern) * 1e3:.2f} us")
         result["exact_decode_ref"] = {
             "us_per_step": round(ems * 1e3, 3),
+            "eager_us_per_step": round(ems_eager * 1e3, 3),
             "GB/s": round(eb["total"] / (ems * 1e-3) / 1e9, 1),
             "pct_of_hbm_peak": round(100 * eb["total"] / (ems * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
             "partial_kernel_us": round(float(np.mean(ekern)) * 1e3, 3),

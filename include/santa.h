@@ -80,12 +80,13 @@ typedef struct {
                                  above max_seq_len are clamped to it.              */
     int32_t q_dtype;          /* santa_dtype; must equal kv_dtype                  */
     int32_t kv_dtype;         /* santa_dtype                                       */
-    int32_t page_size;        /* 0: contiguous K/V.  Else a multiple of 16 and a
-                                 divisor of tile_len: paged pools                  */
+    int32_t page_size;        /* 0: contiguous K/V.  Else a multiple of 16: paged
+                                 pools                                             */
     const int32_t *page_table;/* device [B, max_pages_per_seq] (paged only)        */
     int32_t max_pages_per_seq;/* >= ceil(max_seq_len / page_size) (paged only)     */
     float scale;              /* softmax scale, normally (float)(1/sqrt(d))        */
-    int32_t tile_len;         /* T, tokens per tile: multiple of 64, 64..1024      */
+    int32_t tile_len;         /* T, tokens per tile: 64, 128, 256, 512 or 1024;
+                                 ceil(max_seq_len / T) must not exceed 1024        */
 } santa_problem;
 
 /*
@@ -106,7 +107,7 @@ int santa_workspace_size(const santa_problem *p, int32_t variant, int32_t S, siz
  * S_t > 0, inverts its CDF at its thresholds, gathers those V rows and
  * divides the sum by S.  This equals untiled systematic sampling.
  *
- *   S            samples per head, 1 <= S <= 65536
+ *   S            samples per head, 1 <= S <= 4096 (larger: SANTA_ERR_UNSUPPORTED)
  *   u            [B*Hq] offsets in [0, 1/S) (not checked on the device)
  *   out          [B, Hq, d] fp32 estimate
  *   sample_idx   [B, Hq, S] int32 or NULL: token selected by threshold m,

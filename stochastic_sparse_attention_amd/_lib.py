@@ -11,7 +11,9 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsanta.so")
+# SANTA_LIB selects another build of the same ABI (e.g. a comparison build);
+# by default the in-tree library is loaded
+LIB_PATH = os.environ.get("SANTA_LIB") or os.path.join(HERE, "libsanta.so")
 
 SANTA_OK, SANTA_ERR_INVALID, SANTA_ERR_UNSUPPORTED, SANTA_ERR_WORKSPACE, SANTA_ERR_HIP = 0, -1, -2, -3, -4
 SANTA_F32, SANTA_BF16 = 0, 1

@@ -12,8 +12,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsanta.so")
 ARCH = os.environ.get("SANTA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["santa_kernels.hip", "santa_api.cpp"]
-HEADERS = ["santa_device.h", "santa_score.h", "santa_launch.h"]
+SOURCES = ["santa_prop.hip", "santa_flash.hip", "santa_exact.hip", "santa_api.cpp"]
+HEADERS = ["santa_device.h", "santa_score.h", "santa_launch.h", "santa_kernels.h"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -28,13 +28,18 @@ def _hipcc():
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose=False, jobs=2):
-    objdir = os.path.join(HERE, "_build")
+def build(verbose=False, jobs=4, out=None, defines=()):
+    """Compile every source and link libsanta.so (or `out`).  `defines` adds
+    preprocessor switches, e.g. ("SANTA_BF16_VALU",) builds the VALU scorer
+    for bf16 instead of MFMA (used only for comparisons)."""
+    lib = out or LIB
+    objdir = os.path.join(HERE, "_build", "-".join(defines) or "default")
     os.makedirs(objdir, exist_ok=True)
+    dflags = [f"-D{d}" for d in defines]
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        cmd = [_hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [_hipcc(), *COMMON, *dflags, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,14 +49,20 @@ def build(verbose=False, jobs=2):
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-v", action="store_true")
+    ap.add_argument("--out", default=None)
+    ap.add_argument("-D", action="append", default=[], dest="defines")
+    a = ap.parse_args()
+    print(build(verbose=a.v, out=a.out, defines=tuple(a.defines)))

@@ -11,7 +11,8 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kHeadDimBuilt = 128;
-constexpr int kMaxTiles = 4096;       // merge keeps one fp64 weight per tile in LDS
+constexpr int kMaxTiles = 1024;       // reducer and merge: one thread per tile
+constexpr int kMaxSamplesProp = 4096; // prop keeps the selected rows of a head in LDS
 constexpr int kMaxSamples = 65536;
 
 thread_local void *g_ev_begin = nullptr;
@@ -22,8 +23,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Derived {
     int group = 0;
     int max_nt = 0;
-    int kmax = 0;
-    int nwg = 0;
+    int kmax = 0;   // prop: capacity of the per-head visit list, min(S, n_t)
 };
 
 bool tile_len_built(int T) { return T == 64 || T == 128 || T == 256 || T == 512 || T == 1024; }
@@ -59,17 +59,21 @@ int validate(const santa_problem *p, int variant, int S, Derived *d) {
     if (variant != SANTA_VARIANT_EXACT) {
         if (S < 1 || S > kMaxSamples) return SANTA_ERR_INVALID;
     }
+    if (variant == SANTA_VARIANT_PROP && S > kMaxSamplesProp) return SANTA_ERR_UNSUPPORTED;
     if (variant == SANTA_VARIANT_FLASH) {
         if (p->seq_lens) return SANTA_ERR_INVALID;
         if (S % nt) return SANTA_ERR_INVALID;
+        if (S / nt > p->tile_len) return SANTA_ERR_UNSUPPORTED;   // local list lives in the tile's LDS
     }
     d->group = G;
     d->max_nt = (int)nt;
     d->kmax = (variant == SANTA_VARIANT_PROP) ? (S < nt ? S : (int)nt) : 0;
-    int nwg = (d->kmax + 7) / 8;
-    d->nwg = nwg < 1 ? 1 : (nwg > 8 ? 8 : nwg);
     return SANTA_OK;
 }
+
+// stash rows are padded to a multiple of the tile length (aligned wide
+// stores, and whole-tile reads stay inside the row)
+int stash_stride(const santa_problem *p) { return (p->max_seq_len + p->tile_len - 1) / p->tile_len * p->tile_len; }
 
 // Workspace layout (each region 256-byte aligned).  With base == nullptr it
 // only sizes.
@@ -83,12 +87,8 @@ size_t carve(const santa_problem *p, int variant, const Derived &d, char *base, 
     };
     santa::Workspace w{};
     if (variant == SANTA_VARIANT_PROP) {
-        w.stash = take(BH * (size_t)p->max_seq_len * sizeof(float));
+        w.stash = take(BH * (size_t)stash_stride(p) * sizeof(float));
         w.stats = take(BH * (size_t)d.max_nt * 2 * sizeof(float));
-        w.vis = take(BH * (size_t)d.kmax * santa::visit_record_bytes());
-        w.vis_count = take(BH * sizeof(int));
-        w.counters = take(BH * sizeof(int));
-        w.part = take(BH * (size_t)(4 * d.nwg) * kHeadDimBuilt * sizeof(float));
     } else {
         w.part_m = take(BH * (size_t)d.max_nt * sizeof(float));
         w.part_l = take(BH * (size_t)d.max_nt * sizeof(float));
@@ -133,7 +133,7 @@ santa::LaunchArgs make_args(const santa_problem *p, const Derived &d, const void
     a.sample_idx = sample_idx;
     a.tile_budget = tile_budget;
     a.kmax = d.kmax;
-    a.nwg = d.nwg;
+    a.stash_stride = stash_stride(p);
     a.ws = ws;
     a.stream = stream;
     return a;

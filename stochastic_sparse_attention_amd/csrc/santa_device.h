@@ -5,6 +5,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 namespace santa {
@@ -68,6 +69,27 @@ __device__ __forceinline__ float dpp_f(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+// row_ror:n rotates within each row of 16 lanes
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+}
+// sum / max over the 16 lanes of a DPP row; every lane of the row gets it
+__device__ __forceinline__ float row16_sum(float v) {
+    v += row_ror<8>(v);
+    v += row_ror<4>(v);
+    v += row_ror<2>(v);
+    v += row_ror<1>(v);
+    return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, row_ror<8>(v));
+    v = fmaxf(v, row_ror<4>(v));
+    v = fmaxf(v, row_ror<2>(v));
+    v = fmaxf(v, row_ror<1>(v));
+    return v;
+}
+
 // sum over the 4 lanes of a quad; every lane of the quad gets the result
 __device__ __forceinline__ float quad_sum(float v) {
     v += dpp_f<kQuadXor1>(v);
@@ -82,65 +104,107 @@ __device__ __forceinline__ double quad_sum(double v) {
 }
 
 // ---------------------------------------------------------------- reductions
-// Reductions over the 16 lanes that share (lane & 3): strides 4..32.
+// Reductions over the 16 lanes that share (lane & 3): strides 4 and 8
+// inside a row by DPP rotation, then across the 4 rows.
 __device__ __forceinline__ float sum_stride4(float v) {
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
+    v += row_ror<8>(v);
+    v += row_ror<4>(v);
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
     return v;
 }
 __device__ __forceinline__ float max_stride4(float v) {
-    v = fmaxf(v, __shfl_xor(v, 4));
-    v = fmaxf(v, __shfl_xor(v, 8));
+    v = fmaxf(v, row_ror<8>(v));
+    v = fmaxf(v, row_ror<4>(v));
     v = fmaxf(v, __shfl_xor(v, 16));
     v = fmaxf(v, __shfl_xor(v, 32));
     return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+// ---------------------------------------------------------------- DPP wave scans
+// Inclusive scans over the 64 lanes with DPP only (no LDS round trips):
+// row_shr 1, 2, 4, 8 scan each row of 16 lanes, then row_bcast:15 (rows 1
+// and 3 add the total of the row before) and row_bcast:31 (rows 2 and 3
+// add the total of rows 0-1).  Lanes with no DPP source keep the identity.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp_i(int ident, int v) {
+    return __builtin_amdgcn_update_dpp(ident, v, CTRL, ROWMASK, 0xF, false);
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_f(float ident, float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(ident), __float_as_int(v), CTRL, ROWMASK,
+                                                      0xF, false));
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_d(double ident, double v) {
+    const long long iv = __double_as_longlong(v), ii = __double_as_longlong(ident);
+    const int lo = __builtin_amdgcn_update_dpp((int)ii, (int)iv, CTRL, ROWMASK, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp((int)(ii >> 32), (int)(iv >> 32), CTRL, ROWMASK, 0xF, false);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+__device__ __forceinline__ float wave_incl_scan(float v, int /*lane*/) {
+    v += dpp_f<kRowShr1, 0xF>(0.f, v);
+    v += dpp_f<kRowShr2, 0xF>(0.f, v);
+    v += dpp_f<kRowShr4, 0xF>(0.f, v);
+    v += dpp_f<kRowShr8, 0xF>(0.f, v);
+    v += dpp_f<kRowBcast15, 0xA>(0.f, v);
+    v += dpp_f<kRowBcast31, 0xC>(0.f, v);
     return v;
 }
-__device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) v = max(v, __shfl_xor(v, o));
+__device__ __forceinline__ double wave_incl_scan(double v, int /*lane*/) {
+    v += dpp_d<kRowShr1, 0xF>(0.0, v);
+    v += dpp_d<kRowShr2, 0xF>(0.0, v);
+    v += dpp_d<kRowShr4, 0xF>(0.0, v);
+    v += dpp_d<kRowShr8, 0xF>(0.0, v);
+    v += dpp_d<kRowBcast15, 0xA>(0.0, v);
+    v += dpp_d<kRowBcast31, 0xC>(0.0, v);
+    return v;
+}
+__device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/) {
+    v += dpp_i<kRowShr1, 0xF>(0, v);
+    v += dpp_i<kRowShr2, 0xF>(0, v);
+    v += dpp_i<kRowShr4, 0xF>(0, v);
+    v += dpp_i<kRowShr8, 0xF>(0, v);
+    v += dpp_i<kRowBcast15, 0xA>(0, v);
+    v += dpp_i<kRowBcast31, 0xC>(0, v);
+    return v;
+}
+// running maximum of ints >= 0 (identity 0 ... callers pass non-negative values)
+__device__ __forceinline__ int wave_incl_max_scan(int v, int /*lane*/) {
+    v = max(v, dpp_i<kRowShr1, 0xF>(INT_MIN, v));
+    v = max(v, dpp_i<kRowShr2, 0xF>(INT_MIN, v));
+    v = max(v, dpp_i<kRowShr4, 0xF>(INT_MIN, v));
+    v = max(v, dpp_i<kRowShr8, 0xF>(INT_MIN, v));
+    v = max(v, dpp_i<kRowBcast15, 0xA>(INT_MIN, v));
+    v = max(v, dpp_i<kRowBcast31, 0xC>(INT_MIN, v));
+    return v;
+}
+__device__ __forceinline__ float wave_incl_max_scan(float v) {
+    v = fmaxf(v, dpp_f<kRowShr1, 0xF>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kRowShr2, 0xF>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kRowShr4, 0xF>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kRowShr8, 0xF>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kRowBcast15, 0xA>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kRowBcast31, 0xC>(-INFINITY, v));
     return v;
 }
 
-// Inclusive prefix sum over the wave (Hillis-Steele, fixed order).
-__device__ __forceinline__ float wave_incl_scan(float v, int lane) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        float t = __shfl_up(v, o);
-        if (lane >= o) v += t;
-    }
-    return v;
+// wave-wide maximum, returned to every lane (lane 63 of the scan holds it)
+__device__ __forceinline__ float wave_max(float v) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_incl_max_scan(v)), 63));
 }
-__device__ __forceinline__ double wave_incl_scan(double v, int lane) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        double t = __shfl_up(v, o);
-        if (lane >= o) v += t;
-    }
-    return v;
+__device__ __forceinline__ int wave_max(int v) {
+    return __builtin_amdgcn_readlane(wave_incl_max_scan(v, 0), 63);
 }
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int t = __shfl_up(v, o);
-        if (lane >= o) v += t;
-    }
-    return v;
-}
-__device__ __forceinline__ int wave_incl_max_scan(int v, int lane) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int t = __shfl_up(v, o);
-        if (lane >= o) v = max(v, t);
-    }
-    return v;
+
+// value of lane l-1 (lane 0 gets `first`)
+__device__ __forceinline__ float wave_shift_up(float v, float first) {
+    float u = __shfl_up(v, 1);
+    return (threadIdx.x & 63) ? u : first;
 }
 
 __device__ __forceinline__ void wave_sync_lds() {

@@ -1,0 +1,155 @@
+// santa_exact.hip -- exact split-KV decode kernel and launcher (the baseline).
+//
+// The method follows the web page "Stochastic Sparse Attention for
+// Memory-Bound Inference" (ICML 2026 paper notes on SANTA):
+//   key design 1  systematic sampling: one offset U in [0,1/S), thresholds
+//                 U + m/S, selected index = inverse CDF at each threshold
+//   key design 2  S2ANTA-prop: pass 1 scores and stashes exp-scores with the
+//                 tile partition function, a reducer turns the n_t tile
+//                 masses into per-tile budgets, pass 2 samples and gathers V
+//   key design 3  S2ANTA-flash: S/n_t local samples per tile, partial means
+//                 rescaled by the true tile mass when merged
+// The exact split-KV decode is the FlashDecoding-style baseline the pages
+// compare against.
+//
+// Precision plan (why index parity with an fp64 oracle holds): scores are
+// accumulated unscaled (bf16 products are exact in fp32; fp32 inputs use
+// fp64), the tile max is subtracted before the scale is applied, the reducer
+// works in fp64, and the CDF positions of pass 2 are formed in fp64.
+#include "santa_kernels.h"
+
+namespace santa {
+
+// ===================================================================
+// Exact split-KV decode: per tile (m_t, l_t, o_t = sum_j p_j V_j)
+// ===================================================================
+template <typename KV, int G, int T, bool PAGED>
+__global__ __launch_bounds__(kBlock) void exact_partial_kernel(
+    const KV *__restrict__ q, const KV *__restrict__ k, const KV *__restrict__ v, KVLayout L,
+    const int *__restrict__ seq_lens, int num_q_heads, int max_nt, float scale,
+    float *__restrict__ part_m, float *__restrict__ part_l, float *__restrict__ part_o) {
+    typedef typename ScorerFor<KV, G, T, PAGED>::type SC;
+    typedef typename SC::acc_t acc_t;
+    // tile-fastest numbering: consecutive blocks stream consecutive tiles of
+    // one KV head (adjacent 64 KiB pieces of K for T = 256)
+    const int tile = blockIdx.x % max_nt;
+    const int bg = blockIdx.x / max_nt;
+    const int b = bg / L.num_kv_heads, g = bg - b * L.num_kv_heads;
+    const int n = seq_len_of(seq_lens, L.max_seq_len, b);
+    const int t0 = tile * T;
+    if (t0 >= n) return;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+
+    SC sc;
+    sc.load_q(q + ((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim);
+    sc.score(k, L, b, g, t0, n);
+
+    __shared__ float red_m[kWavesPerBlock][16];
+    __shared__ float red_l[kWavesPerBlock][16];
+    __shared__ float Pw[G][T];
+    __shared__ float red_o[kWavesPerBlock][G][kHeadDim];
+    float mt[SC::NV];
+    tile_max(sc, red_m, mt);
+    const acc_t c2 = (acc_t)scale * (acc_t)1.4426950408889634;
+#pragma unroll
+    for (int v = 0; v < SC::NV; ++v) {
+        const int hl = SC::head(lane, v);
+        float lsum = 0.f;
+        if (hl < G) {
+#pragma unroll
+            for (int s = 0; s < SC::NS; ++s) {
+                const int row = SC::row(lane, w, s);
+                const float p = (t0 + row < n) ? exp_weight(sc.x[s][v], mt[v], c2) : 0.f;
+                Pw[hl][row] = p;
+                lsum += p;
+            }
+        }
+        lsum = SC::reduce_sum(lsum);
+        if (SC::writer(lane) && hl < 16) red_l[w][hl] = lsum;
+    }
+    __syncthreads();
+
+    // V pass: 16 lanes per row (8 elements each), 4 rows per wave step,
+    // 16 consecutive rows per block step
+    const int slot = lane >> 4, chunk = lane & 15;
+    float acc[G][8];
+#pragma unroll
+    for (int hl = 0; hl < G; ++hl)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[hl][e] = 0.f;
+#pragma unroll 4
+    for (int i2 = 0; i2 < T / 16; ++i2) {
+        const int row = 16 * i2 + 4 * w + slot;
+        if (t0 + row < n) {
+            float xv[8];
+            load_v8<KV>(v + row_offset(L, b, g, t0 + row) + 8 * chunk, xv);
+#pragma unroll
+            for (int hl = 0; hl < G; ++hl) {
+                const float p = Pw[hl][row];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[hl][e] = fmaf(p, xv[e], acc[hl][e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int hl = 0; hl < G; ++hl)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            acc[hl][e] += __shfl_xor(acc[hl][e], 16);
+            acc[hl][e] += __shfl_xor(acc[hl][e], 32);
+        }
+    if (lane < 16) {
+#pragma unroll
+        for (int hl = 0; hl < G; ++hl)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red_o[w][hl][8 * chunk + e] = acc[hl][e];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kBlock) {
+        const int hl = idx / kHeadDim, d = idx - hl * kHeadDim;
+        float s = red_o[0][hl][d];
+#pragma unroll
+        for (int ww = 1; ww < kWavesPerBlock; ++ww) s += red_o[ww][hl][d];
+        const size_t bh = (size_t)b * num_q_heads + (size_t)g * G + hl;
+        part_o[(bh * max_nt + tile) * kHeadDim + d] = s;
+    }
+    if (threadIdx.x < G) {
+        const int hl = threadIdx.x;
+        float m = red_m[0][hl], l = red_l[0][hl];
+#pragma unroll
+        for (int ww = 1; ww < kWavesPerBlock; ++ww) {
+            m = fmaxf(m, red_m[ww][hl]);
+            l += red_l[ww][hl];
+        }
+        const size_t bh = (size_t)b * num_q_heads + (size_t)g * G + hl;
+        part_m[bh * max_nt + tile] = m;
+        part_l[bh * max_nt + tile] = l;
+    }
+}
+
+// ===================================================================
+// launchers
+// ===================================================================
+template <typename KV, int G, int T, bool PAGED>
+static hipError_t launch_exact_t(const LaunchArgs &a, const TimingHook &hook) {
+    hipStream_t st = (hipStream_t)a.stream;
+    const KVLayout L = layout_of(a);
+    const int max_nt = a.max_nt;
+    if (hook.begin) hipEventRecord((hipEvent_t)hook.begin, st);
+    hipLaunchKernelGGL((exact_partial_kernel<KV, G, T, PAGED>),
+                       dim3((unsigned)(a.batch * a.num_kv_heads * max_nt)), dim3(kBlock), 0, st,
+                       (const KV *)a.q, (const KV *)a.k, (const KV *)a.v, L, a.seq_lens, a.num_q_heads,
+                       max_nt, a.scale, (float *)a.ws.part_m, (float *)a.ws.part_l, (float *)a.ws.part_o);
+    if (hook.end) hipEventRecord((hipEvent_t)hook.end, st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(merge_tiles_kernel, dim3((unsigned)(a.batch * a.num_q_heads)), dim3(kMergeBlock),
+                       sizeof(double) * (size_t)max_nt, st, (const float *)a.ws.part_m,
+                       (const float *)a.ws.part_l, (const float *)a.ws.part_o, a.seq_lens, a.max_seq_len, T,
+                       max_nt, a.batch, a.num_q_heads, a.num_kv_heads, 0, a.scale, a.out);
+    return hipGetLastError();
+}
+
+hipError_t launch_exact(const LaunchArgs &a, const TimingHook &hook) { SANTA_DISPATCH(launch_exact_t) }
+
+}  // namespace santa

@@ -1,0 +1,180 @@
+// santa_flash.hip -- S2ANTA-flash tile kernel and launcher.
+//
+// The method follows the web page "Stochastic Sparse Attention for
+// Memory-Bound Inference" (ICML 2026 paper notes on SANTA):
+//   key design 1  systematic sampling: one offset U in [0,1/S), thresholds
+//                 U + m/S, selected index = inverse CDF at each threshold
+//   key design 2  S2ANTA-prop: pass 1 scores and stashes exp-scores with the
+//                 tile partition function, a reducer turns the n_t tile
+//                 masses into per-tile budgets, pass 2 samples and gathers V
+//   key design 3  S2ANTA-flash: S/n_t local samples per tile, partial means
+//                 rescaled by the true tile mass when merged
+// The exact split-KV decode is the FlashDecoding-style baseline the pages
+// compare against.
+//
+// Precision plan (why index parity with an fp64 oracle holds): scores are
+// accumulated unscaled (bf16 products are exact in fp32; fp32 inputs use
+// fp64), the tile max is subtracted before the scale is applied, the reducer
+// works in fp64, and the CDF positions of pass 2 are formed in fp64.
+#include "santa_kernels.h"
+
+namespace santa {
+
+// ===================================================================
+// S2ANTA-flash: tile kernel (score, local softmax, S_f local samples,
+// gather) -- merge below
+// ===================================================================
+// part_m / part_z [B, Hq, nt] (unscaled tile max, local partition function)
+// part_o [B, Hq, nt, d]: mean of the tile's S_f sampled V rows
+//
+// Local sampling per head (one wave): inclusive scan of the tile's weights,
+// local thresholds u_f + m/S_f on the local CDF P_j / Z_t with u_f = U * n_t,
+// and the same per-element count rule as pass 2 of prop (counts of
+// thresholds below each position, monotone, forced to S_f from the last
+// nonzero weight on).
+template <typename KV, int G, int T, bool PAGED>
+__global__ __launch_bounds__(kBlock) void flash_tile_kernel(
+    const KV *__restrict__ q, const KV *__restrict__ k, const KV *__restrict__ v, KVLayout L,
+    int num_q_heads, int nt, int Sf, int S, float scale, const float *__restrict__ u,
+    float *__restrict__ part_m, float *__restrict__ part_z, float *__restrict__ part_o,
+    int *__restrict__ sample_idx) {
+    typedef typename ScorerFor<KV, G, T, PAGED>::type SC;
+    typedef typename SC::acc_t acc_t;
+    constexpr int EPL = T / 64;
+    // tile-fastest numbering: consecutive blocks stream consecutive tiles of
+    // one KV head (adjacent 64 KiB pieces of K for T = 256)
+    const int tile = blockIdx.x % nt;
+    const int bg = blockIdx.x / nt;
+    const int b = bg / L.num_kv_heads, g = bg - b * L.num_kv_heads;
+    const int n = L.max_seq_len;
+    const int t0 = tile * T;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+
+    SC sc;
+    sc.load_q(q + ((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim);
+    sc.score(k, L, b, g, t0, n);
+
+    __shared__ float red_m[kWavesPerBlock][16];
+    __shared__ float E[G][T];
+    float mt[SC::NV];
+    tile_max(sc, red_m, mt);
+    const acc_t c2 = (acc_t)scale * (acc_t)1.4426950408889634;
+#pragma unroll
+    for (int v = 0; v < SC::NV; ++v) {
+        const int hl = SC::head(lane, v);
+        if (hl < G) {
+#pragma unroll
+            for (int s = 0; s < SC::NS; ++s) {
+                const int row = SC::row(lane, w, s);
+                E[hl][row] = (t0 + row < n) ? exp_weight(sc.x[s][v], mt[v], c2) : 0.f;
+            }
+        }
+    }
+    __syncthreads();
+
+    for (int hl = w; hl < G; hl += kWavesPerBlock) {
+        const int bh = b * num_q_heads + g * G + hl;
+        float e[EPL];
+        int lz = -1;
+        float run = 0.f;
+#pragma unroll
+        for (int qq = 0; qq < EPL; ++qq) {
+            e[qq] = E[hl][lane * EPL + qq];
+            if (e[qq] > 0.f) lz = lane * EPL + qq;
+            run += e[qq];
+            e[qq] = run;
+        }
+        lz = wave_max(lz);
+        const float lincl = wave_incl_scan(run, lane);
+        float excl = __shfl_up(lincl, 1);
+        if (lane == 0) excl = 0.f;
+        const float Zt = __shfl(lincl, 63);
+        const double uf = (double)u[bh] * (double)nt;
+        // per-element local threshold counts #{m : u_f + m/S_f < P_j / Z_t}
+        int cj[EPL];
+        int lmax = 0;
+#pragma unroll
+        for (int qq = 0; qq < EPL; ++qq) {
+            const int j = lane * EPL + qq;
+            int cc = Sf;
+            if (j < lz) cc = thresholds_below((double)(excl + e[qq]) / (double)Zt, uf, Sf);
+            lmax = max(lmax, cc);
+            cj[qq] = lmax;
+        }
+        const int lmax_incl = wave_incl_max_scan(lmax, lane);
+        int pmax = __shfl_up(lmax_incl, 1);
+        if (lane == 0) pmax = 0;
+        // selected rows of this head go to an LDS list that reuses E[hl]
+        // (S_f <= T is checked on the host), after every lane has read it
+        wave_sync_lds();
+        int *sel = reinterpret_cast<int *>(&E[hl][0]);
+        int prev = pmax;
+#pragma unroll
+        for (int qq = 0; qq < EPL; ++qq) {
+            const int cc = max(cj[qq], pmax);
+            for (int m = prev; m < cc; ++m) sel[m] = t0 + lane * EPL + qq;
+            prev = cc;
+        }
+        wave_sync_lds();
+        if (sample_idx)
+            for (int m = lane; m < Sf; m += 64) sample_idx[(size_t)bh * S + (size_t)tile * Sf + m] = sel[m];
+        // gather S_f rows: 16 lanes per row, 4 rows per instruction
+        const int slot = lane >> 4, chunk = lane & 15;
+        float acc[8];
+#pragma unroll
+        for (int ee = 0; ee < 8; ++ee) acc[ee] = 0.f;
+#pragma unroll 4
+        for (int m = slot; m < Sf; m += 4) {
+            float xv[8];
+            load_v8<KV>(v + row_offset(L, b, g, sel[m]) + 8 * chunk, xv);
+#pragma unroll
+            for (int ee = 0; ee < 8; ++ee) acc[ee] += xv[ee];
+        }
+#pragma unroll
+        for (int ee = 0; ee < 8; ++ee) {
+            acc[ee] += __shfl_xor(acc[ee], 16);
+            acc[ee] += __shfl_xor(acc[ee], 32);
+        }
+        const bool pow2 = (Sf & (Sf - 1)) == 0;
+        if (lane < 16) {
+            float *dst = part_o + ((size_t)bh * nt + tile) * kHeadDim + 8 * lane;
+#pragma unroll
+            for (int ee = 0; ee < 8; ++ee) dst[ee] = pow2 ? acc[ee] * (1.0f / (float)Sf) : acc[ee] / (float)Sf;
+        }
+        if (lane == 0) {
+            float m = red_m[0][hl];
+#pragma unroll
+            for (int ww = 1; ww < kWavesPerBlock; ++ww) m = fmaxf(m, red_m[ww][hl]);
+            part_m[(size_t)bh * nt + tile] = m;
+            part_z[(size_t)bh * nt + tile] = Zt;
+        }
+    }
+}
+
+// ===================================================================
+// launchers
+// ===================================================================
+template <typename KV, int G, int T, bool PAGED>
+static hipError_t launch_flash_t(const LaunchArgs &a, const TimingHook &hook) {
+    hipStream_t st = (hipStream_t)a.stream;
+    const KVLayout L = layout_of(a);
+    const int nt = a.max_nt;
+    if (hook.begin) hipEventRecord((hipEvent_t)hook.begin, st);
+    hipLaunchKernelGGL((flash_tile_kernel<KV, G, T, PAGED>),
+                       dim3((unsigned)(a.batch * a.num_kv_heads * nt)), dim3(kBlock), 0, st,
+                       (const KV *)a.q, (const KV *)a.k, (const KV *)a.v, L, a.num_q_heads, nt, a.S / nt,
+                       a.S, a.scale, a.u, (float *)a.ws.part_m, (float *)a.ws.part_l, (float *)a.ws.part_o,
+                       a.sample_idx);
+    if (hook.end) hipEventRecord((hipEvent_t)hook.end, st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(merge_tiles_kernel, dim3((unsigned)(a.batch * a.num_q_heads)), dim3(kMergeBlock),
+                       sizeof(double) * (size_t)nt, st, (const float *)a.ws.part_m,
+                       (const float *)a.ws.part_l, (const float *)a.ws.part_o, (const int *)nullptr,
+                       a.max_seq_len, T, nt, a.batch, a.num_q_heads, a.num_kv_heads, 1, a.scale, a.out);
+    return hipGetLastError();
+}
+
+hipError_t launch_flash(const LaunchArgs &a, const TimingHook &hook) { SANTA_DISPATCH(launch_flash_t) }
+
+}  // namespace santa

@@ -10,12 +10,8 @@ namespace santa {
 
 // Carved workspace regions (device pointers; unused ones are null).
 struct Workspace {
-    void *stash;      // prop: [B, Hq, max_seq_len] fp32
+    void *stash;      // prop: [B, Hq, stash_stride] fp32
     void *stats;      // prop: [B, Hq, max_nt] float2
-    void *vis;        // prop: [B, Hq, kmax] visit records
-    void *vis_count;  // prop: [B, Hq] int32
-    void *counters;   // prop: [B, Hq] int32 pass-2 arrival tickets
-    void *part;       // prop: [B, Hq, 4*nwg, d] fp32 wave partial sums
     void *part_m;     // flash/exact: [B, Hq, max_nt] fp32
     void *part_l;     // flash/exact: [B, Hq, max_nt] fp32
     void *part_o;     // flash/exact: [B, Hq, max_nt, d] fp32
@@ -37,7 +33,7 @@ struct LaunchArgs {
     int *sample_idx;
     int *tile_budget;
     int kmax;   // prop: visit-list capacity per head
-    int nwg;    // prop: pass-2 workgroups per head
+    int stash_stride;   // prop: floats per stash row (max_seq_len rounded up to T)
     Workspace ws;
     void *stream;
 };

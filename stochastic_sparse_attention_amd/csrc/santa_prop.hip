@@ -1,0 +1,398 @@
+// santa_prop.hip -- S2ANTA-prop kernels (pass 1; reducer + pass 2) and launcher.
+//
+// The method follows the web page "Stochastic Sparse Attention for
+// Memory-Bound Inference" (ICML 2026 paper notes on SANTA):
+//   key design 1  systematic sampling: one offset U in [0,1/S), thresholds
+//                 U + m/S, selected index = inverse CDF at each threshold
+//   key design 2  S2ANTA-prop: pass 1 scores and stashes exp-scores with the
+//                 tile partition function, a reducer turns the n_t tile
+//                 masses into per-tile budgets, pass 2 samples and gathers V
+//   key design 3  S2ANTA-flash: S/n_t local samples per tile, partial means
+//                 rescaled by the true tile mass when merged
+// The exact split-KV decode is the FlashDecoding-style baseline the pages
+// compare against.
+//
+// Precision plan (why index parity with an fp64 oracle holds): scores are
+// accumulated unscaled (bf16 products are exact in fp32; fp32 inputs use
+// fp64), the tile max is subtracted before the scale is applied, the reducer
+// works in fp64, and the CDF positions of pass 2 are formed in fp64.
+#include "santa_kernels.h"
+
+namespace santa {
+
+// ===================================================================
+// S2ANTA-prop, pass 1: scores, tile max, tile partition function, stash
+// ===================================================================
+// grid: B * Hkv * max_nt workgroups (tile fastest); block: 256 threads.
+// stash [B, Hq, max_seq_len] fp32: e_j = exp(scale * (x_j - m_t))
+// stats [B, Hq, max_nt] float2: (m_t unscaled tile max, Z_t = sum_j e_j)
+template <typename KV, int G, int T, bool PAGED>
+__global__ __launch_bounds__(kBlock) void prop_pass1_kernel(
+    const KV *__restrict__ q, const KV *__restrict__ k, KVLayout L, const int *__restrict__ seq_lens,
+    int num_q_heads, int max_nt, float scale, float *__restrict__ stash, int stash_stride,
+    float2 *__restrict__ stats) {
+    typedef typename ScorerFor<KV, G, T, PAGED>::type SC;
+    typedef typename SC::acc_t acc_t;
+    // tile-fastest numbering: consecutive blocks stream consecutive tiles of
+    // one KV head (adjacent 64 KiB pieces of K for T = 256)
+    const int tile = blockIdx.x % max_nt;
+    const int bg = blockIdx.x / max_nt;
+    const int b = bg / L.num_kv_heads, g = bg - b * L.num_kv_heads;
+    const int n = seq_len_of(seq_lens, L.max_seq_len, b);
+    const int t0 = tile * T;
+    if (t0 >= n) return;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+
+    SC sc;
+    sc.load_q(q + ((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim);
+    sc.score(k, L, b, g, t0, n);
+
+    __shared__ float red_m[kWavesPerBlock][16];
+    __shared__ float red_z[kWavesPerBlock][16];
+    __shared__ __align__(16) float E[G][T];           // the tile's stash rows, staged for wide stores
+    float mt[SC::NV];
+    tile_max(sc, red_m, mt);
+
+    const acc_t c2 = (acc_t)scale * (acc_t)1.4426950408889634;   // scale * log2(e)
+#pragma unroll
+    for (int v = 0; v < SC::NV; ++v) {
+        const int hl = SC::head(lane, v);                 // head within the group
+        float zsum = 0.f;
+        if (hl < G) {
+#pragma unroll
+            for (int s = 0; s < SC::NS; ++s) {
+                const int row = SC::row(lane, w, s);
+                const float e = (t0 + row < n) ? exp_weight(sc.x[s][v], mt[v], c2) : 0.f;
+                E[hl][row] = e;
+                zsum += e;
+            }
+        }
+        zsum = SC::reduce_sum(zsum);
+        if (SC::writer(lane) && hl < 16) red_z[w][hl] = zsum;
+    }
+    __syncthreads();
+    // stash: wave w writes head rows w, w+4, ...; each store instruction
+    // covers 64 lanes x 16 bytes = 256 consecutive tokens
+    const int len = min(T, n - t0);
+    for (int hl = w; hl < G; hl += kWavesPerBlock) {
+        float *srow = stash + ((size_t)b * num_q_heads + (size_t)g * G + hl) * (size_t)stash_stride + t0;
+#pragma unroll
+        for (int j4 = 4 * lane; j4 < T; j4 += 256) {
+            if (j4 + 3 < len) {
+                *reinterpret_cast<float4 *>(srow + j4) = *reinterpret_cast<const float4 *>(&E[hl][j4]);
+            } else {
+                for (int jj = j4; jj < len; ++jj) srow[jj] = E[hl][jj];
+            }
+        }
+    }
+    if (threadIdx.x < G) {
+        const int hl = threadIdx.x;
+        float z = red_z[0][hl], m = red_m[0][hl];
+#pragma unroll
+        for (int ww = 1; ww < kWavesPerBlock; ++ww) {
+            z += red_z[ww][hl];
+            m = fmaxf(m, red_m[ww][hl]);
+        }
+        stats[((size_t)b * num_q_heads + (size_t)g * G + hl) * max_nt + tile] = make_float2(m, z);
+    }
+}
+
+// ===================================================================
+// S2ANTA-prop, reducer + pass 2: one 1024-thread workgroup per (request,
+// q head).  No cross-workgroup communication.
+// ===================================================================
+// Reducer (thread t <-> tile t; n_t <= 1024): global max M of the tile
+// maxima, tile masses z_t = Z_t e^{scale (m_t - M)}, Z = sum z_t, tile CDF
+// C_t (fp64, C_{n_t-1} := 1), threshold counts cnt_t = #{m : U + m/S < C_t}
+// made monotone, budgets S_t = cnt_t - cnt_{t-1}; tiles with S_t > 0 go to
+// an LDS visit list in tile order.
+// Pass 2 (one wave per visited tile): inclusive scan of the tile's stash,
+// CDF positions F_j = C_{t-1} + P_j e^{scale (m_t - M)} / Z, per-element
+// counts c_j = #{m : t_m < F_j} clamped to the tile's threshold range and
+// forced to its end from the last token of nonzero weight on, made
+// monotone; token j takes thresholds c_{j-1} .. c_j - 1 (its multiplicity
+// is c_j - c_{j-1}), written to an LDS list of selected rows.
+// Gather: the S selected rows are read (16 lanes per row, 4 rows per wave
+// instruction), summed in a fixed order and divided by S.
+struct VisitRec {
+    int t, first, cnt, pad;
+    double cprev, r;
+};
+
+constexpr int kMaxTilesLds = 1024;   // tiles per request the reducer keeps in LDS
+
+// EPL consecutive floats from a 16-byte aligned address (EPL = T/64)
+template <int EPL>
+__device__ __forceinline__ void load_stash(const float *p, float (&e)[EPL]) {
+    if constexpr (EPL >= 4) {
+#pragma unroll
+        for (int i = 0; i < EPL; i += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(p + i);
+            e[i] = v.x; e[i + 1] = v.y; e[i + 2] = v.z; e[i + 3] = v.w;
+        }
+    } else if constexpr (EPL == 2) {
+        const float2 v = *reinterpret_cast<const float2 *>(p);
+        e[0] = v.x; e[1] = v.y;
+    } else {
+        e[0] = p[0];
+    }
+}
+
+template <typename KV, int T, bool PAGED>
+__global__ __launch_bounds__(kSampleBlock) void prop_sample_kernel(
+    const KV *__restrict__ v, KVLayout L, const int *__restrict__ seq_lens, int batch, int num_q_heads,
+    int G, int S, int max_nt, int kcap, const float *__restrict__ u, float scale,
+    const float *__restrict__ stash, int stash_stride, const float2 *__restrict__ stats, float *__restrict__ out,
+    int *__restrict__ sample_idx, int *__restrict__ tile_budget) {
+    constexpr int EPL = T / 64;
+    constexpr int NB = 4;                            // visited tiles per wave whose stash loads overlap
+    extern __shared__ __align__(16) unsigned char smem[];
+    VisitRec *vis = reinterpret_cast<VisitRec *>(smem);                  // [kcap]
+    int *jsel = reinterpret_cast<int *>(smem + (size_t)kcap * sizeof(VisitRec));   // [S]
+    __shared__ float red[kSampleWaves][kHeadDim];
+    __shared__ float2 tstat[kMaxTilesLds];          // reducer: per-tile (m_t, Z_t)
+    __shared__ double tf[kMaxTilesLds];             // reducer: e^{scale (m_t - M)}
+    __shared__ double tC[kMaxTilesLds];             // reducer: tile CDF C_t
+    __shared__ int nvis_sh;
+
+    // block -> (request, KV head, head in group); blocks of one KV head are
+    // numbered bg + i * B*Hkv, the numbering pass 1 uses for that head's tiles
+    const int BG = batch * L.num_kv_heads;
+    const int bg = blockIdx.x % BG, hl = blockIdx.x / BG;
+    const int b = bg / L.num_kv_heads, g = bg - b * L.num_kv_heads;
+    const int bh = b * num_q_heads + g * G + hl;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n = seq_len_of(seq_lens, L.max_seq_len, b);
+    const int nt = (n + T - 1) / T;
+
+    if (nt == 0) {                                  // empty request
+        if (tile_budget)
+            for (int t = tid; t < max_nt; t += kSampleBlock) tile_budget[(size_t)bh * max_nt + t] = 0;
+        if (sample_idx)
+            for (int m = tid; m < S; m += kSampleBlock) sample_idx[(size_t)bh * S + m] = -1;
+        if (tid < kHeadDim) out[(size_t)bh * kHeadDim + tid] = 0.f;
+        return;
+    }
+    const double U = (double)u[bh];
+
+    // ---------------- reducer: wave 0, lane l owns tiles [l*CH, l*CH + CH)
+    if (w == 0) {
+        const int CH = (nt + 63) / 64;
+        const int tb = lane * CH, te = min(nt, tb + CH);
+        const float2 *stp = stats + (size_t)bh * max_nt;
+        float lmaxv = -INFINITY;
+        for (int t = tb; t < te; ++t) {
+            const float2 v2 = stp[t];
+            tstat[t] = v2;
+            lmaxv = fmaxf(lmaxv, v2.x);
+        }
+        const float Mf = wave_max(lmaxv);
+        // tile weight e^{scale (m_t - M)} in fp32: its rounding moves a tile's
+        // CDF interval by ~1e-7 of the tile's own mass, and the same value is
+        // used for C_t and for the pass-2 mapping, so the two stay consistent
+        const float c2 = scale * 1.4426950408889634f;
+        double lsum = 0.0;
+        for (int t = tb; t < te; ++t) {
+            const float2 v2 = tstat[t];
+            const double f = (double)exp2f((v2.x - Mf) * c2);
+            tf[t] = f;
+            lsum += (double)v2.y * f;
+        }
+        const double incl = wave_incl_scan(lsum, lane);
+        double excl = __shfl_up(incl, 1);
+        if (lane == 0) excl = 0.0;
+        const double Z = __shfl(incl, 63);
+        // C_t = (excl + lane-local running sum) / Z, C_{n_t-1} := 1; counts
+        // of thresholds below each C_t, made monotone across lanes
+        double lrun = 0.0;
+        int lcnt = 0;
+        for (int t = tb; t < te; ++t) {
+            lrun += (double)tstat[t].y * tf[t];
+            const double C = (t == nt - 1) ? 1.0 : (excl + lrun) / Z;
+            tC[t] = C;
+            lcnt = max(lcnt, thresholds_below(C, U, S));
+        }
+        const int cmax = wave_incl_max_scan(lcnt, lane);
+        int cpred = __shfl_up(cmax, 1);
+        double Cpred = __shfl_up(te > tb ? tC[te - 1] : 0.0, 1);      // C of the previous lane's last tile
+        if (lane == 0) {
+            cpred = 0;
+            Cpred = 0.0;
+        }
+        // visited tiles of this lane, then their positions in the visit list
+        int nvl = 0;
+        {
+            int cp = cpred;
+            for (int t = tb; t < te; ++t) {
+                const int cnt = max(cp, thresholds_below(tC[t], U, S));
+                nvl += cnt > cp;
+                cp = cnt;
+            }
+        }
+        const int vincl = wave_incl_scan(nvl, lane);
+        int vpos = vincl - nvl;
+        if (lane == 63) nvis_sh = vincl;
+        {
+            int cp = cpred;
+            double cprev = Cpred;
+            for (int t = tb; t < te; ++t) {
+                const int cnt = max(cp, thresholds_below(tC[t], U, S));
+                const int St = cnt - cp;
+                if (tile_budget) tile_budget[(size_t)bh * max_nt + t] = St;
+                if (St > 0 && vpos < kcap) {
+                    VisitRec rec;
+                    rec.t = t;
+                    rec.first = cp;
+                    rec.cnt = St;
+                    rec.pad = 0;
+                    rec.cprev = cprev;
+                    rec.r = tf[t] / Z;
+                    vis[vpos] = rec;
+                    ++vpos;
+                }
+                cp = cnt;
+                cprev = tC[t];
+            }
+        }
+        if (tile_budget)
+            for (int t = nt + lane; t < max_nt; t += 64) tile_budget[(size_t)bh * max_nt + t] = 0;
+    }
+    __syncthreads();
+    const int nvis = min(nvis_sh, kcap);
+
+    // ---------------- pass 2: per visited tile, threshold counts -> jsel
+    for (int k0 = w; k0 < nvis; k0 += NB * kSampleWaves) {
+        VisitRec rec[NB];
+        float e[NB][EPL];
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi) {           // issue the stash loads of up to NB tiles
+            const int kv = k0 + bi * kSampleWaves;
+            rec[bi] = vis[kv < nvis ? kv : k0];
+            // whole tile, unconditionally: stash rows are padded to a multiple
+            // of T, so the read stays inside the row; rows past the end are
+            // zeroed by the select below
+            const float *sp = stash + (size_t)bh * stash_stride + rec[bi].t * T + lane * EPL;
+            load_stash<EPL>(sp, e[bi]);
+        }
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi) {
+            const int len = min(T, n - rec[bi].t * T);
+#pragma unroll
+            for (int qq = 0; qq < EPL; ++qq) e[bi][qq] = (lane * EPL + qq < len) ? e[bi][qq] : 0.f;
+        }
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi) {
+            const int kv = k0 + bi * kSampleWaves;
+            if (kv >= nvis) break;
+            const int start = rec[bi].t * T;
+            int lz = -1;
+            float run = 0.f;
+#pragma unroll
+            for (int qq = 0; qq < EPL; ++qq) {
+                if (e[bi][qq] > 0.f) lz = lane * EPL + qq;
+                run += e[bi][qq];
+                e[bi][qq] = run;                       // in-lane inclusive prefix
+            }
+            lz = wave_max(lz);
+            const float lincl = wave_incl_scan(run, lane);
+            float excl = __shfl_up(lincl, 1);
+            if (lane == 0) excl = 0.f;
+            const int lo = rec[bi].first, hi = rec[bi].first + rec[bi].cnt;
+            int cj[EPL];
+            int lmax = lo;
+#pragma unroll
+            for (int qq = 0; qq < EPL; ++qq) {
+                const int j = lane * EPL + qq;
+                int cc = hi;
+                if (j < lz) {
+                    const double F = rec[bi].cprev + (double)(excl + e[bi][qq]) * rec[bi].r;
+                    cc = thresholds_below(F, U, S);
+                    cc = cc < lo ? lo : (cc > hi ? hi : cc);
+                }
+                lmax = max(lmax, cc);
+                cj[qq] = lmax;                             // in-lane running max
+            }
+            const int lmax_incl = wave_incl_max_scan(lmax, lane);   // running max from earlier lanes
+            int pmax = __shfl_up(lmax_incl, 1);
+            if (lane == 0) pmax = lo;
+            int prev = pmax;
+#pragma unroll
+            for (int qq = 0; qq < EPL; ++qq) {
+                const int cc = max(cj[qq], pmax);
+                for (int m = prev; m < cc; ++m) jsel[m] = start + lane * EPL + qq;
+                prev = cc;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---------------- gather the S selected rows
+    const int slot = lane >> 4, chunk = lane & 15;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll 4
+    for (int m = 4 * w + slot; m < S; m += 4 * kSampleWaves) {
+        const int row = jsel[m];
+        float xv[8];
+        load_v8<KV>(v + row_offset(L, b, g, row) + 8 * chunk, xv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += xv[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        acc[e] += __shfl_xor(acc[e], 16);
+        acc[e] += __shfl_xor(acc[e], 32);
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[w][8 * chunk + e] = acc[e];
+    }
+    if (sample_idx)
+        for (int m = tid; m < S; m += kSampleBlock) sample_idx[(size_t)bh * S + m] = jsel[m];
+    __syncthreads();
+    if (tid < kHeadDim) {
+        float sum = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kSampleWaves; ++ww) sum += red[ww][tid];
+        // divide by S: for a power of two this is an exact exponent shift
+        const bool pow2 = (S & (S - 1)) == 0;
+        out[(size_t)bh * kHeadDim + tid] = pow2 ? sum * (1.0f / (float)S) : sum / (float)S;
+    }
+}
+
+// ===================================================================
+// launchers
+// ===================================================================
+size_t prop_sample_lds_bytes(int kcap, int S) {
+    return (size_t)kcap * sizeof(VisitRec) + (size_t)S * sizeof(int);
+}
+
+template <typename KV, int G, int T, bool PAGED>
+static hipError_t launch_prop_t(const LaunchArgs &a, const TimingHook &hook) {
+    const int max_nt = a.max_nt;
+    hipStream_t st = (hipStream_t)a.stream;
+    float *stash = (float *)a.ws.stash;
+    float2 *stats = (float2 *)a.ws.stats;
+    const KVLayout L = layout_of(a);
+    if (hook.begin) hipEventRecord((hipEvent_t)hook.begin, st);
+    hipLaunchKernelGGL((prop_pass1_kernel<KV, G, T, PAGED>),
+                       dim3((unsigned)(a.batch * a.num_kv_heads * max_nt)), dim3(kBlock), 0, st,
+                       (const KV *)a.q, (const KV *)a.k, L, a.seq_lens, a.num_q_heads, max_nt, a.scale,
+                       stash, a.stash_stride, stats);
+    if (hook.end) hipEventRecord((hipEvent_t)hook.end, st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int BH = a.batch * a.num_q_heads;
+    hipLaunchKernelGGL((prop_sample_kernel<KV, T, PAGED>), dim3((unsigned)BH), dim3(kSampleBlock),
+                       prop_sample_lds_bytes(a.kmax, a.S), st, (const KV *)a.v, L, a.seq_lens, a.batch,
+                       a.num_q_heads, G, a.S, max_nt, a.kmax, a.u, a.scale, (const float *)stash,
+                       a.stash_stride, (const float2 *)stats, a.out, a.sample_idx, a.tile_budget);
+    return hipGetLastError();
+}
+
+hipError_t launch_prop(const LaunchArgs &a, const TimingHook &hook) { SANTA_DISPATCH(launch_prop_t) }
+
+size_t visit_record_bytes() { return sizeof(VisitRec); }
+
+}  // namespace santa

@@ -1,56 +1,34 @@
 // santa_score.h -- streaming the K tile of one (request, KV head) and scoring
 // it for every query head of the group.
 //
-// Thread layout of a 256-thread workgroup over a tile of T rows (T % 64 == 0):
-//   wave w (0..3), lane l; quad position c = l & 3, row slot r = l >> 2 (0..15)
-//   step i (0..T/64-1) covers tile rows 64*i + 16*w + r, so the 4 waves of one
-//   step read 64 consecutive rows (16 KiB of bf16 K).  Within a row the 4
-//   lanes of a quad each read 16-byte chunks c, c+4, c+8, ... (coalesced
-//   64-byte pieces; 4 per bf16 row, 8 per fp32 row).
-//   Every lane forms partial dot products over its part of the row for all
-//   G heads; a quad sum completes them.  Lane c then keeps heads c, c+4, ...
+// A 256-thread workgroup scores a tile of T rows (T % 64 == 0): wave w,
+// step s (0..T/64-1) covers the 16 consecutive tile rows 64 s + 16 w + 0..15,
+// so the 4 waves of one step read 64 consecutive rows.  Two lane layouts:
+//
+//  * MFMA (bf16 K): the group's queries are the A operand of
+//    v_mfma_f32_16x16x32_bf16 (16 rows = heads, padded with zeros), 16 K rows
+//    are the B operand (16 columns = tokens), 4 MFMAs cover d = 128.  Lane l
+//    loads 16 bytes of token l%16 at d = 32 kb + 8 (l/16) for kb = 0..3 and
+//    receives the scores of heads 4 (l/16) + v, v = 0..3, for that token.
+//    Each token's 256-byte row is read as four 64-byte pieces per MFMA step.
+//  * VALU (fp32 K, fp64 accumulation; also bf16 when SANTA_BF16_VALU is
+//    defined, for comparison): 4 lanes per row, each holding 16-byte chunks
+//    c, c+4, ... of the row; partial dots for every head, a quad sum, then
+//    lane c keeps heads c + 4 v.
 //
 // Scores are kept UNSCALED (x = <q, k>); the softmax scale is applied after
-// the max subtraction, which keeps the large planted-key logits exact to the
-// accumulation error only.  bf16 inputs accumulate in fp32 (bf16 products
-// are exact in fp32); fp32 inputs accumulate in fp64.
+// the max subtraction, which keeps large planted-key logits accurate to the
+// accumulation error.  bf16 products are exact in fp32; fp32 inputs use fp64.
 #pragma once
 
 #include "santa_device.h"
 
 namespace santa {
 
-template <typename KV> struct KVTraits;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-template <> struct KVTraits<uint16_t> {       // bf16 storage
-    typedef float acc_t;
-    static constexpr int kChunks = kHeadDim * 2 / 64;   // 16-byte chunks per lane per row
-};
-template <> struct KVTraits<float> {
-    typedef double acc_t;
-    static constexpr int kChunks = kHeadDim * 4 / 64;
-};
-
-template <int G> struct HeadsPerLane { static constexpr int value = (G + 3) / 4; };
-
-// q fragment of one lane: the elements of its row chunks, for all G heads
-template <typename KV, int G>
-struct QFrag {
-    u32x4 v[G][KVTraits<KV>::kChunks];
-};
-
-template <typename KV, int G>
-__device__ __forceinline__ void load_qfrag(QFrag<KV, G> &f, const KV *q_group, int c) {
-    constexpr int NC = KVTraits<KV>::kChunks;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(q_group);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int j = 0; j < NC; ++j)
-            f.v[h][j] = src[h * (kHeadDim * sizeof(KV) / 16) + c + 4 * j];
-}
-
-// partial dot of one chunk pair (16 bytes of q and 16 bytes of k)
+// partial dot of one 16-byte chunk pair
 __device__ __forceinline__ float chunk_dot(const u32x4 &a, const u32x4 &b, float acc) {
     acc = dot2_bf16(a.x, b.x, acc);
     acc = dot2_bf16(a.y, b.y, acc);
@@ -66,50 +44,202 @@ __device__ __forceinline__ double chunk_dot(const u32x4 &a, const u32x4 &b, doub
     return acc;
 }
 
-// Score the tile rows [t0, t0 + T) of (b, g), rows >= n are invalid.
-// x[i][hh]: unscaled score of row t0 + 64 i + 16 w + r for head c + 4 hh,
-// or -inf when the row is invalid or the head index is >= G.
-template <typename KV, int G, int T>
-__device__ __forceinline__ void score_tile(
-    const KV *__restrict__ k, const KVLayout &L, int b, int g, int t0, int n,
-    const QFrag<KV, G> &qf, typename KVTraits<KV>::acc_t (&x)[T / 64][HeadsPerLane<G>::value]) {
+// wave-uniform element offset of the 16-row block starting at row j0; a
+// block starting at or past n (end of the request) is replaced by the
+// tile's first block, which is valid since t0 < n, so every load stays in
+// bounds without a branch (scores of such rows are masked by the caller)
+template <bool PAGED>
+__device__ __forceinline__ size_t block_base(const KVLayout &L, int b, int g, int j0, int n, int t0) {
+    const int jb = j0 < n ? j0 : t0;
+    if (PAGED) {
+        const int page = L.page_table[(size_t)b * L.max_pages + jb / L.page_size];
+        return ((size_t)(page * L.num_kv_heads + g) * L.page_size + (jb % L.page_size)) * kHeadDim;
+    }
+    return ((size_t)(b * L.num_kv_heads + g) * L.max_seq_len + jb) * kHeadDim;
+}
+
+// ------------------------------------------------------------------ MFMA
+template <int G, int T, bool PAGED>
+struct ScorerMfma {
+    typedef float acc_t;
+    static constexpr int NS = T / 64;
+    static constexpr int NV = 4;
+    static constexpr int CH = NS < 4 ? NS : 4;   // steps whose K loads are in flight together
+    bf16x8_t qa[4];
+    acc_t x[NS][NV];
+
+    __device__ __forceinline__ static int head(int lane, int v) { return 4 * (lane >> 4) + v; }
+    __device__ __forceinline__ static int row(int lane, int w, int s) { return 64 * s + 16 * w + (lane & 15); }
+    __device__ __forceinline__ static bool writer(int lane) { return (lane & 15) == 0; }
+    __device__ __forceinline__ static float reduce_max(float v) { return row16_max(v); }
+    __device__ __forceinline__ static float reduce_sum(float v) { return row16_sum(v); }
+
+    __device__ __forceinline__ void load_q(const uint16_t *q_group) {
+        const int lane = threadIdx.x & 63;
+        const int hrow = lane & 15, kq = lane >> 4;
+        // rows >= G repeat row G-1: their MFMA outputs are never used, and the
+        // load stays unconditional (no branch, so no early wait on it)
+        const int hsrc = hrow < G ? hrow : G - 1;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            qa[kb] = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const u32x4 *>(q_group + hsrc * kHeadDim + 32 * kb + 8 * kq));
+    }
+
+    __device__ __forceinline__ void score(const uint16_t *__restrict__ k, const KVLayout &L, int b, int g,
+                                          int t0, int n) {
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        const int tok = lane & 15, kq = lane >> 4;
+#pragma unroll
+        for (int s0 = 0; s0 < NS; s0 += CH) {
+            size_t base[CH];
+#pragma unroll
+            for (int ii = 0; ii < CH; ++ii) base[ii] = block_base<PAGED>(L, b, g, t0 + 64 * (s0 + ii) + 16 * w, n, t0);
+            u32x4 kv[CH][4];
+#pragma unroll
+            for (int ii = 0; ii < CH; ++ii) {
+                // rows past the end read the block's row 0 (always a valid row
+                // of the tile); their scores are masked below
+                const bool valid = t0 + 64 * (s0 + ii) + 16 * w + tok < n;
+                const u32x4 *rowp =
+                    reinterpret_cast<const u32x4 *>(k + base[ii] + (size_t)(valid ? tok : 0) * kHeadDim) + kq;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) kv[ii][kb] = __builtin_nontemporal_load(rowp + 4 * kb);
+            }
+#pragma unroll
+            for (int ii = 0; ii < CH; ++ii) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], __builtin_bit_cast(bf16x8_t, kv[ii][kb]),
+                                                                  acc, 0, 0, 0);
+                const bool valid = t0 + 64 * (s0 + ii) + 16 * w + tok < n;
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+                    x[s0 + ii][v] = (valid && head(lane, v) < G) ? acc[v] : -INFINITY;
+            }
+        }
+    }
+};
+
+// ------------------------------------------------------------------ VALU
+template <typename KV> struct KVTraits;
+template <> struct KVTraits<uint16_t> {       // bf16 storage
+    typedef float acc_t;
+    static constexpr int kChunks = kHeadDim * 2 / 64;   // 16-byte chunks per lane per row
+};
+template <> struct KVTraits<float> {
+    typedef double acc_t;
+    static constexpr int kChunks = kHeadDim * 4 / 64;
+};
+
+template <typename KV, int G, int T, bool PAGED>
+struct ScorerValu {
     typedef typename KVTraits<KV>::acc_t acc_t;
-    constexpr int NC = KVTraits<KV>::kChunks;
-    constexpr int HPL = HeadsPerLane<G>::value;
+    static constexpr int NC = KVTraits<KV>::kChunks;
+    static constexpr int NS = T / 64;
+    static constexpr int NV = (G + 3) / 4;            // heads per lane
+    // steps whose K loads are in flight together (keeps G >= 4 under 128 VGPRs)
+    static constexpr int CHMAX = G <= 2 ? 4 : 2;
+    static constexpr int CH = NS < CHMAX ? NS : CHMAX;
+    static constexpr int ROW_VEC = kHeadDim * (int)sizeof(KV) / 16;
+    u32x4 qv[G][NC];
+    acc_t x[NS][NV];
+
+    __device__ __forceinline__ static int head(int lane, int v) { return (lane & 3) + 4 * v; }
+    __device__ __forceinline__ static int row(int lane, int w, int s) { return 64 * s + 16 * w + (lane >> 2); }
+    __device__ __forceinline__ static bool writer(int lane) { return lane < 4; }
+    __device__ __forceinline__ static float reduce_max(float v) { return max_stride4(v); }
+    __device__ __forceinline__ static float reduce_sum(float v) { return sum_stride4(v); }
+
+    __device__ __forceinline__ void load_q(const KV *q_group) {
+        const int c = threadIdx.x & 3;
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(q_group);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int j = 0; j < NC; ++j) qv[h][j] = src[h * ROW_VEC + c + 4 * j];
+    }
+
+    __device__ __forceinline__ void score(const KV *__restrict__ k, const KVLayout &L, int b, int g, int t0,
+                                          int n) {
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        const int c = lane & 3, r = lane >> 2;
+#pragma unroll
+        for (int s0 = 0; s0 < NS; s0 += CH) {
+            size_t base[CH];
+#pragma unroll
+            for (int ii = 0; ii < CH; ++ii) base[ii] = block_base<PAGED>(L, b, g, t0 + 64 * (s0 + ii) + 16 * w, n, t0);
+            u32x4 kv[CH][NC];
+#pragma unroll
+            for (int ii = 0; ii < CH; ++ii) {
+                const bool valid = t0 + 64 * (s0 + ii) + 16 * w + r < n;
+                const u32x4 *rowp = reinterpret_cast<const u32x4 *>(k + base[ii]) + (valid ? r : 0) * ROW_VEC;
+#pragma unroll
+                for (int jj = 0; jj < NC; ++jj) kv[ii][jj] = __builtin_nontemporal_load(rowp + c + 4 * jj);
+            }
+#pragma unroll
+            for (int ii = 0; ii < CH; ++ii) {
+                const bool valid = t0 + 64 * (s0 + ii) + 16 * w + r < n;
+                acc_t part[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    acc_t a = 0;
+#pragma unroll
+                    for (int jj = 0; jj < NC; ++jj) a = chunk_dot(qv[h][jj], kv[ii][jj], a);
+                    part[h] = quad_sum(a);
+                }
+#pragma unroll
+                for (int hh = 0; hh < NV; ++hh) {
+                    acc_t s = part[hh * 4 < G ? hh * 4 : 0];
+#pragma unroll
+                    for (int h = hh * 4 + 1; h < G && h < hh * 4 + 4; ++h)
+                        if (c == h - hh * 4) s = part[h];
+                    x[s0 + ii][hh] = (valid && head(lane, hh) < G) ? s : (acc_t)(-INFINITY);
+                }
+            }
+        }
+    }
+};
+
+// scorer used for a storage type: MFMA for bf16, VALU/fp64 for fp32
+template <typename KV, int G, int T, bool PAGED> struct ScorerFor;
+template <int G, int T, bool PAGED> struct ScorerFor<float, G, T, PAGED> {
+    typedef ScorerValu<float, G, T, PAGED> type;
+};
+#ifdef SANTA_BF16_VALU
+template <int G, int T, bool PAGED> struct ScorerFor<uint16_t, G, T, PAGED> {
+    typedef ScorerValu<uint16_t, G, T, PAGED> type;
+};
+#else
+template <int G, int T, bool PAGED> struct ScorerFor<uint16_t, G, T, PAGED> {
+    typedef ScorerMfma<G, T, PAGED> type;
+};
+#endif
+
+// Per-head tile maximum of the unscaled scores: red_m[w][head] holds each
+// wave's maximum, mt[v] the tile maximum of this lane's v-th head.
+template <class SC>
+__device__ __forceinline__ void tile_max(const SC &sc, float (&red_m)[kWavesPerBlock][16],
+                                         float (&mt)[SC::NV]) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int c = lane & 3, r = lane >> 2;
 #pragma unroll
-    for (int i = 0; i < T / 64; ++i) {
-        const int j0 = t0 + 64 * i + 16 * w;          // first row of this wave's block
-        const bool valid = (j0 + r) < n;
-        u32x4 kv[NC];
-        if (j0 < n) {
-            const u32x4 *row = reinterpret_cast<const u32x4 *>(k + block16_offset(L, b, g, j0)) +
-                               (size_t)r * (kHeadDim * sizeof(KV) / 16);
+    for (int v = 0; v < SC::NV; ++v) {
+        typename SC::acc_t m = sc.x[0][v];
 #pragma unroll
-            for (int jj = 0; jj < NC; ++jj)
-                kv[jj] = valid ? __builtin_nontemporal_load(row + c + 4 * jj) : u32x4{0u, 0u, 0u, 0u};
-        } else {
+        for (int s = 1; s < SC::NS; ++s) m = sc.x[s][v] > m ? sc.x[s][v] : m;
+        const float mf = SC::reduce_max((float)m);
+        const int h = SC::head(lane, v);
+        if (SC::writer(lane) && h < 16) red_m[w][h] = mf;
+    }
+    __syncthreads();
 #pragma unroll
-            for (int jj = 0; jj < NC; ++jj) kv[jj] = u32x4{0u, 0u, 0u, 0u};
-        }
-        acc_t part[G];
+    for (int v = 0; v < SC::NV; ++v) {
+        const int h = SC::head(lane, v) & 15;
+        float m = red_m[0][h];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            acc_t a = 0;
-#pragma unroll
-            for (int jj = 0; jj < NC; ++jj) a = chunk_dot(qf.v[h][jj], kv[jj], a);
-            part[h] = quad_sum(a);
-        }
-#pragma unroll
-        for (int hh = 0; hh < HPL; ++hh) {
-            acc_t s = part[hh * 4 < G ? hh * 4 : 0];
-#pragma unroll
-            for (int h = hh * 4 + 1; h < G && h < hh * 4 + 4; ++h)
-                if (c == h - hh * 4) s = part[h];
-            const bool head_ok = (c + 4 * hh) < G;
-            x[i][hh] = (valid && head_ok) ? s : (acc_t)(-INFINITY);
-        }
+        for (int ww = 1; ww < kWavesPerBlock; ++ww) m = fmaxf(m, red_m[ww][h]);
+        mt[v] = m;
     }
 }
 
