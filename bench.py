@@ -145,6 +145,9 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-exact", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 5 device copies of 256 MiB (known traffic: 256 MiB read and "
+                         "256 MiB written each) to calibrate the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="graph: steps replayed from a captured HIP graph (value); "
                          "eager: one host call per step")
@@ -157,6 +160,14 @@ def main(argv=None):
         return 2
 
     import torch
+    if args.copy_calibration:
+        a = torch.full((256 << 20,), 3, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("bench: 5 copies of 256 MiB done")
+        return 0
     import stochastic_sparse_attention_amd as sa
     from stochastic_sparse_attention_amd import bytemodel as BM
     from stochastic_sparse_attention_amd import synth

@@ -193,6 +193,32 @@ __device__ __forceinline__ float wave_incl_max_scan(float v) {
     return v;
 }
 
+// Inclusive scans over groups of LPT consecutive lanes (LPT = 16, 32 or 64):
+// the row steps, then the row_bcast steps that stay inside a group.
+template <int LPT>
+__device__ __forceinline__ float group_incl_scan(float v) {
+    v += dpp_f<kRowShr1, 0xF>(0.f, v);
+    v += dpp_f<kRowShr2, 0xF>(0.f, v);
+    v += dpp_f<kRowShr4, 0xF>(0.f, v);
+    v += dpp_f<kRowShr8, 0xF>(0.f, v);
+    if (LPT >= 32) v += dpp_f<kRowBcast15, 0xA>(0.f, v);
+    if (LPT >= 64) v += dpp_f<kRowBcast31, 0xC>(0.f, v);
+    return v;
+}
+template <int LPT>
+__device__ __forceinline__ int group_incl_max(int v) {
+    v = max(v, dpp_i<kRowShr1, 0xF>(INT_MIN, v));
+    v = max(v, dpp_i<kRowShr2, 0xF>(INT_MIN, v));
+    v = max(v, dpp_i<kRowShr4, 0xF>(INT_MIN, v));
+    v = max(v, dpp_i<kRowShr8, 0xF>(INT_MIN, v));
+    if (LPT >= 32) v = max(v, dpp_i<kRowBcast15, 0xA>(INT_MIN, v));
+    if (LPT >= 64) v = max(v, dpp_i<kRowBcast31, 0xC>(INT_MIN, v));
+    return v;
+}
+// value of the lane LPT-1 of this lane's group (the group's inclusive total)
+template <int LPT>
+__device__ __forceinline__ int group_last_lane(int lane) { return (lane | (LPT - 1)); }
+
 // wave-wide maximum, returned to every lane (lane 63 of the scan holds it)
 __device__ __forceinline__ float wave_max(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_incl_max_scan(v)), 63));
@@ -213,12 +239,12 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// count of thresholds t_m = U + m/S (m = 0..S-1) strictly below x
+// count of thresholds t_m = U + m/S (m = 0..S-1) strictly below x:
+// #{m >= 0 : m < (x - U) S} = ceil((x - U) S), clamped to [0, S]
+// (branch-free; a NaN position counts as 0)
 __device__ __forceinline__ int thresholds_below(double x, double U, int S) {
-    double c = ceil((x - U) * (double)S);
-    if (!(c > 0.0)) return 0;
-    if (c > (double)S) return S;
-    return (int)c;
+    const double c = ceil((x - U) * (double)S);
+    return (int)fmin(fmax(c, 0.0), (double)S);
 }
 
 }  // namespace santa

@@ -135,12 +135,16 @@ static hipError_t launch_exact_t(const LaunchArgs &a, const TimingHook &hook) {
     hipStream_t st = (hipStream_t)a.stream;
     const KVLayout L = layout_of(a);
     const int max_nt = a.max_nt;
-    if (hook.begin) hipEventRecord((hipEvent_t)hook.begin, st);
-    hipLaunchKernelGGL((exact_partial_kernel<KV, G, T, PAGED>),
-                       dim3((unsigned)(a.batch * a.num_kv_heads * max_nt)), dim3(kBlock), 0, st,
+    // with a timing hook the dispatch itself records the two events, so
+    // they bracket the kernel's execution and nothing else
+    if (hook.begin)
+        hipExtLaunchKernelGGL((exact_partial_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * max_nt)), dim3(kBlock), 0, st, (hipEvent_t)hook.begin, (hipEvent_t)hook.end, 0,
                        (const KV *)a.q, (const KV *)a.k, (const KV *)a.v, L, a.seq_lens, a.num_q_heads,
                        max_nt, a.scale, (float *)a.ws.part_m, (float *)a.ws.part_l, (float *)a.ws.part_o);
-    if (hook.end) hipEventRecord((hipEvent_t)hook.end, st);
+    else
+        hipLaunchKernelGGL((exact_partial_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * max_nt)), dim3(kBlock), 0, st,
+                       (const KV *)a.q, (const KV *)a.k, (const KV *)a.v, L, a.seq_lens, a.num_q_heads,
+                       max_nt, a.scale, (float *)a.ws.part_m, (float *)a.ws.part_l, (float *)a.ws.part_o);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(merge_tiles_kernel, dim3((unsigned)(a.batch * a.num_q_heads)), dim3(kMergeBlock),

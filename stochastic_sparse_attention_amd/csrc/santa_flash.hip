@@ -159,13 +159,18 @@ static hipError_t launch_flash_t(const LaunchArgs &a, const TimingHook &hook) {
     hipStream_t st = (hipStream_t)a.stream;
     const KVLayout L = layout_of(a);
     const int nt = a.max_nt;
-    if (hook.begin) hipEventRecord((hipEvent_t)hook.begin, st);
-    hipLaunchKernelGGL((flash_tile_kernel<KV, G, T, PAGED>),
-                       dim3((unsigned)(a.batch * a.num_kv_heads * nt)), dim3(kBlock), 0, st,
+    // with a timing hook the dispatch itself records the two events, so
+    // they bracket the kernel's execution and nothing else
+    if (hook.begin)
+        hipExtLaunchKernelGGL((flash_tile_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * nt)), dim3(kBlock), 0, st, (hipEvent_t)hook.begin, (hipEvent_t)hook.end, 0,
                        (const KV *)a.q, (const KV *)a.k, (const KV *)a.v, L, a.num_q_heads, nt, a.S / nt,
                        a.S, a.scale, a.u, (float *)a.ws.part_m, (float *)a.ws.part_l, (float *)a.ws.part_o,
                        a.sample_idx);
-    if (hook.end) hipEventRecord((hipEvent_t)hook.end, st);
+    else
+        hipLaunchKernelGGL((flash_tile_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * nt)), dim3(kBlock), 0, st,
+                       (const KV *)a.q, (const KV *)a.k, (const KV *)a.v, L, a.num_q_heads, nt, a.S / nt,
+                       a.S, a.scale, a.u, (float *)a.ws.part_m, (float *)a.ws.part_l, (float *)a.ws.part_o,
+                       a.sample_idx);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(merge_tiles_kernel, dim3((unsigned)(a.batch * a.num_q_heads)), dim3(kMergeBlock),

@@ -4,6 +4,8 @@
 // dispatch macros.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "santa_launch.h"
 #include "santa_score.h"
 

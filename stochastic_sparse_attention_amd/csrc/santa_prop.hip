@@ -261,66 +261,61 @@ __global__ __launch_bounds__(kSampleBlock) void prop_sample_kernel(
     const int nvis = min(nvis_sh, kcap);
 
     // ---------------- pass 2: per visited tile, threshold counts -> jsel
-    for (int k0 = w; k0 < nvis; k0 += NB * kSampleWaves) {
-        VisitRec rec[NB];
-        float e[NB][EPL];
-#pragma unroll
-        for (int bi = 0; bi < NB; ++bi) {           // issue the stash loads of up to NB tiles
-            const int kv = k0 + bi * kSampleWaves;
-            rec[bi] = vis[kv < nvis ? kv : k0];
-            // whole tile, unconditionally: stash rows are padded to a multiple
-            // of T, so the read stays inside the row; rows past the end are
-            // zeroed by the select below
-            const float *sp = stash + (size_t)bh * stash_stride + rec[bi].t * T + lane * EPL;
-            load_stash<EPL>(sp, e[bi]);
-        }
-#pragma unroll
-        for (int bi = 0; bi < NB; ++bi) {
-            const int len = min(T, n - rec[bi].t * T);
-#pragma unroll
-            for (int qq = 0; qq < EPL; ++qq) e[bi][qq] = (lane * EPL + qq < len) ? e[bi][qq] : 0.f;
-        }
-#pragma unroll
-        for (int bi = 0; bi < NB; ++bi) {
-            const int kv = k0 + bi * kSampleWaves;
-            if (kv >= nvis) break;
-            const int start = rec[bi].t * T;
+    // A wave takes TPW visited tiles at once, LPT lanes per tile, EPL
+    // consecutive stash values per lane (all loads of the wave in flight
+    // together); scans run inside each LPT-lane group.
+    {
+        constexpr int LPT = T >= 1024 ? 64 : (T >= 512 ? 32 : 16);
+        constexpr int TPW = 64 / LPT;
+        constexpr int EPL2 = T / LPT;
+        const int sub = lane / LPT, gl = lane % LPT;          // tile slot in the wave, lane in group
+        for (int k0 = w * TPW; k0 < nvis; k0 += TPW * kSampleWaves) {
+            const int kv = k0 + sub;
+            const bool active = kv < nvis;
+            const VisitRec rec = vis[active ? kv : k0];
+            const int start = rec.t * T;
+            const int len = min(T, n - start);
+            float e[EPL2];
+            // whole slice, unconditionally: stash rows are padded to a multiple
+            // of T, so the read stays inside the row; elements past the end
+            // are zeroed by the select below
+            load_stash<EPL2>(stash + (size_t)bh * stash_stride + start + gl * EPL2, e);
             int lz = -1;
             float run = 0.f;
 #pragma unroll
-            for (int qq = 0; qq < EPL; ++qq) {
-                if (e[bi][qq] > 0.f) lz = lane * EPL + qq;
-                run += e[bi][qq];
-                e[bi][qq] = run;                       // in-lane inclusive prefix
+            for (int qq = 0; qq < EPL2; ++qq) {
+                const int j = gl * EPL2 + qq;
+                const float x = (j < len) ? e[qq] : 0.f;
+                if (x > 0.f) lz = j;
+                run += x;
+                e[qq] = run;                               // in-lane inclusive prefix
             }
-            lz = wave_max(lz);
-            const float lincl = wave_incl_scan(run, lane);
-            float excl = __shfl_up(lincl, 1);
-            if (lane == 0) excl = 0.f;
-            const int lo = rec[bi].first, hi = rec[bi].first + rec[bi].cnt;
-            int cj[EPL];
+            lz = __builtin_amdgcn_ds_bpermute(4 * group_last_lane<LPT>(lane), group_incl_max<LPT>(lz));
+            const float gincl = group_incl_scan<LPT>(run);
+            float excl = __shfl_up(gincl, 1);              // sum of the earlier lanes of the group
+            if (gl == 0) excl = 0.f;
+            const int lo = rec.first, hi = rec.first + rec.cnt;
+            int cj[EPL2];
             int lmax = lo;
 #pragma unroll
-            for (int qq = 0; qq < EPL; ++qq) {
-                const int j = lane * EPL + qq;
-                int cc = hi;
-                if (j < lz) {
-                    const double F = rec[bi].cprev + (double)(excl + e[bi][qq]) * rec[bi].r;
-                    cc = thresholds_below(F, U, S);
-                    cc = cc < lo ? lo : (cc > hi ? hi : cc);
-                }
-                lmax = max(lmax, cc);
-                cj[qq] = lmax;                             // in-lane running max
+            for (int qq = 0; qq < EPL2; ++qq) {
+                const int j = gl * EPL2 + qq;
+                const double F = rec.cprev + (double)(excl + e[qq]) * rec.r;
+                const int cc = min(max(thresholds_below(F, U, S), lo), hi);
+                lmax = max(lmax, j < lz ? cc : hi);    // from the last nonzero weight on: all of the tile's thresholds
+                cj[qq] = lmax;                         // in-lane running max
             }
-            const int lmax_incl = wave_incl_max_scan(lmax, lane);   // running max from earlier lanes
-            int pmax = __shfl_up(lmax_incl, 1);
-            if (lane == 0) pmax = lo;
-            int prev = pmax;
+            const int gmax = group_incl_max<LPT>(lmax);   // running max from earlier lanes of the group
+            int pmax = __shfl_up(gmax, 1);
+            if (gl == 0) pmax = lo;
+            // thresholds pmax .. last-1 fall on this lane's elements; element
+            // qq takes those m with max(c_{qq-1}, pmax) <= m < max(c_qq, pmax)
+            const int last = active ? max(cj[EPL2 - 1], pmax) : pmax;
+            for (int m = pmax; m < last; ++m) {
+                int q = 0;
 #pragma unroll
-            for (int qq = 0; qq < EPL; ++qq) {
-                const int cc = max(cj[qq], pmax);
-                for (int m = prev; m < cc; ++m) jsel[m] = start + lane * EPL + qq;
-                prev = cc;
+                for (int qq = 0; qq < EPL2; ++qq) q += (cj[qq] <= m) ? 1 : 0;
+                jsel[m] = start + gl * EPL2 + q;
             }
         }
     }
@@ -375,12 +370,16 @@ static hipError_t launch_prop_t(const LaunchArgs &a, const TimingHook &hook) {
     float *stash = (float *)a.ws.stash;
     float2 *stats = (float2 *)a.ws.stats;
     const KVLayout L = layout_of(a);
-    if (hook.begin) hipEventRecord((hipEvent_t)hook.begin, st);
-    hipLaunchKernelGGL((prop_pass1_kernel<KV, G, T, PAGED>),
-                       dim3((unsigned)(a.batch * a.num_kv_heads * max_nt)), dim3(kBlock), 0, st,
+    // with a timing hook the dispatch itself records the two events, so
+    // they bracket the kernel's execution and nothing else
+    if (hook.begin)
+        hipExtLaunchKernelGGL((prop_pass1_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * max_nt)), dim3(kBlock), 0, st, (hipEvent_t)hook.begin, (hipEvent_t)hook.end, 0,
                        (const KV *)a.q, (const KV *)a.k, L, a.seq_lens, a.num_q_heads, max_nt, a.scale,
                        stash, a.stash_stride, stats);
-    if (hook.end) hipEventRecord((hipEvent_t)hook.end, st);
+    else
+        hipLaunchKernelGGL((prop_pass1_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * max_nt)), dim3(kBlock), 0, st,
+                       (const KV *)a.q, (const KV *)a.k, L, a.seq_lens, a.num_q_heads, max_nt, a.scale,
+                       stash, a.stash_stride, stats);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int BH = a.batch * a.num_q_heads;
