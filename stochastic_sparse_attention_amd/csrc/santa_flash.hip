@@ -91,14 +91,17 @@ __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
         const float Zt = __shfl(lincl, 63);
         const double uf = (double)u[bh] * (double)nt;
         // per-element local threshold counts #{m : u_f + m/S_f < P_j / Z_t}
+        //   = ceil(P_j * a + b), a = S_f / Z_t, b = -u_f S_f (fp32; the
+        //   rounding moves a threshold by ~1e-7 of the tile's mass)
+        const float a = (float)((double)Sf / (double)Zt), bb = (float)(-uf * (double)Sf);
+        const float fSf = (float)Sf;
         int cj[EPL];
         int lmax = 0;
 #pragma unroll
         for (int qq = 0; qq < EPL; ++qq) {
             const int j = lane * EPL + qq;
-            int cc = Sf;
-            if (j < lz) cc = thresholds_below((double)(excl + e[qq]) / (double)Zt, uf, Sf);
-            lmax = max(lmax, cc);
+            const int cc = (int)fminf(fmaxf(ceilf(fmaf(excl + e[qq], a, bb)), 0.f), fSf);
+            lmax = max(lmax, j < lz ? cc : Sf);
             cj[qq] = lmax;
         }
         const int lmax_incl = wave_incl_max_scan(lmax, lane);

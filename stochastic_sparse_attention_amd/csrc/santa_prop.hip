@@ -114,9 +114,14 @@ __global__ __launch_bounds__(kBlock) void prop_pass1_kernel(
 // is c_j - c_{j-1}), written to an LDS list of selected rows.
 // Gather: the S selected rows are read (16 lanes per row, 4 rows per wave
 // instruction), summed in a fixed order and divided by S.
+// Visit record of a tile with S_t > 0: its thresholds are first .. first+cnt-1
+// and the number of thresholds below the CDF position of its element j is
+// ceil(P_j * a + b), with P_j the stash prefix, a = S e^{scale(m_t-M)}/Z and
+// b = S (C_{t-1} - U) (formed in fp64, rounded to fp32: the rounding moves a
+// threshold by ~1e-7 in CDF units).
 struct VisitRec {
-    int t, first, cnt, pad;
-    double cprev, r;
+    int t, first, cnt;
+    float a, b;
 };
 
 constexpr int kMaxTilesLds = 1024;   // tiles per request the reducer keeps in LDS
@@ -244,9 +249,8 @@ __global__ __launch_bounds__(kSampleBlock) void prop_sample_kernel(
                     rec.t = t;
                     rec.first = cp;
                     rec.cnt = St;
-                    rec.pad = 0;
-                    rec.cprev = cprev;
-                    rec.r = tf[t] / Z;
+                    rec.a = (float)((double)S * (tf[t] / Z));
+                    rec.b = (float)((double)S * (cprev - U));
                     vis[vpos] = rec;
                     ++vpos;
                 }
@@ -297,11 +301,11 @@ __global__ __launch_bounds__(kSampleBlock) void prop_sample_kernel(
             const int lo = rec.first, hi = rec.first + rec.cnt;
             int cj[EPL2];
             int lmax = lo;
+            const float flo = (float)lo, fhi = (float)hi;
 #pragma unroll
             for (int qq = 0; qq < EPL2; ++qq) {
                 const int j = gl * EPL2 + qq;
-                const double F = rec.cprev + (double)(excl + e[qq]) * rec.r;
-                const int cc = min(max(thresholds_below(F, U, S), lo), hi);
+                const int cc = (int)fminf(fmaxf(ceilf(fmaf(excl + e[qq], rec.a, rec.b)), flo), fhi);
                 lmax = max(lmax, j < lz ? cc : hi);    // from the last nonzero weight on: all of the tile's thresholds
                 cj[qq] = lmax;                         // in-lane running max
             }
