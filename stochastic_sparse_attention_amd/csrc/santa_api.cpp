@@ -71,10 +71,6 @@ int validate(const santa_problem *p, int variant, int S, Derived *d) {
     return SANTA_OK;
 }
 
-// stash rows are padded to a multiple of the tile length (aligned wide
-// stores, and whole-tile reads stay inside the row)
-int stash_stride(const santa_problem *p) { return (p->max_seq_len + p->tile_len - 1) / p->tile_len * p->tile_len; }
-
 // Workspace layout (each region 256-byte aligned).  With base == nullptr it
 // only sizes.
 size_t carve(const santa_problem *p, int variant, const Derived &d, char *base, santa::Workspace *ws) {
@@ -87,7 +83,9 @@ size_t carve(const santa_problem *p, int variant, const Derived &d, char *base, 
     };
     santa::Workspace w{};
     if (variant == SANTA_VARIANT_PROP) {
-        w.stash = take(BH * (size_t)stash_stride(p) * sizeof(float));
+        // every tile in full, also the short last one (aligned wide stores,
+        // and whole-tile reads in pass 2)
+        w.stash = take(BH * (size_t)d.max_nt * p->tile_len * sizeof(float));
         w.stats = take(BH * (size_t)d.max_nt * 2 * sizeof(float));
     } else {
         w.part_m = take(BH * (size_t)d.max_nt * sizeof(float));
@@ -133,7 +131,6 @@ santa::LaunchArgs make_args(const santa_problem *p, const Derived &d, const void
     a.sample_idx = sample_idx;
     a.tile_budget = tile_budget;
     a.kmax = d.kmax;
-    a.stash_stride = stash_stride(p);
     a.ws = ws;
     a.stream = stream;
     return a;

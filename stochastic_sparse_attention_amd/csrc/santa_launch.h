@@ -10,7 +10,7 @@ namespace santa {
 
 // Carved workspace regions (device pointers; unused ones are null).
 struct Workspace {
-    void *stash;      // prop: [B, Hq, stash_stride] fp32
+    void *stash;      // prop: [B, Hq, max_nt * T] fp32
     void *stats;      // prop: [B, Hq, max_nt] float2
     void *part_m;     // flash/exact: [B, Hq, max_nt] fp32
     void *part_l;     // flash/exact: [B, Hq, max_nt] fp32
@@ -33,7 +33,6 @@ struct LaunchArgs {
     int *sample_idx;
     int *tile_budget;
     int kmax;   // prop: visit-list capacity per head
-    int stash_stride;   // prop: floats per stash row (max_seq_len rounded up to T)
     Workspace ws;
     void *stream;
 };

@@ -24,13 +24,13 @@ namespace santa {
 // S2ANTA-prop, pass 1: scores, tile max, tile partition function, stash
 // ===================================================================
 // grid: B * Hkv * max_nt workgroups (tile fastest); block: 256 threads.
-// stash [B, Hq, max_seq_len] fp32: e_j = exp(scale * (x_j - m_t))
+// stash [B, Hq, max_nt * T] fp32 (rows padded to whole tiles):
+// e_j = exp(scale * (x_j - m_t))
 // stats [B, Hq, max_nt] float2: (m_t unscaled tile max, Z_t = sum_j e_j)
 template <typename KV, int G, int T, bool PAGED>
 __global__ __launch_bounds__(kBlock) void prop_pass1_kernel(
     const KV *__restrict__ q, const KV *__restrict__ k, KVLayout L, const int *__restrict__ seq_lens,
-    int num_q_heads, int max_nt, float scale, float *__restrict__ stash, int stash_stride,
-    float2 *__restrict__ stats) {
+    int num_q_heads, int max_nt, float scale, float *__restrict__ stash, float2 *__restrict__ stats) {
     typedef typename ScorerFor<KV, G, T, PAGED>::type SC;
     typedef typename SC::acc_t acc_t;
     // tile-fastest numbering: consecutive blocks stream consecutive tiles of
@@ -72,18 +72,14 @@ __global__ __launch_bounds__(kBlock) void prop_pass1_kernel(
     }
     __syncthreads();
     // stash: wave w writes head rows w, w+4, ...; each store instruction
-    // covers 64 lanes x 16 bytes = 256 consecutive tokens
-    const int len = min(T, n - t0);
+    // covers 64 lanes x 16 bytes = 256 consecutive tokens.  The whole tile
+    // is written, so positions past the sequence end hold 0 and pass 2
+    // reads them unmasked.
     for (int hl = w; hl < G; hl += kWavesPerBlock) {
-        float *srow = stash + ((size_t)b * num_q_heads + (size_t)g * G + hl) * (size_t)stash_stride + t0;
+        float *srow = stash + ((size_t)b * num_q_heads + (size_t)g * G + hl) * ((size_t)max_nt * T) + t0;
 #pragma unroll
-        for (int j4 = 4 * lane; j4 < T; j4 += 256) {
-            if (j4 + 3 < len) {
-                *reinterpret_cast<float4 *>(srow + j4) = *reinterpret_cast<const float4 *>(&E[hl][j4]);
-            } else {
-                for (int jj = j4; jj < len; ++jj) srow[jj] = E[hl][jj];
-            }
-        }
+        for (int j4 = 4 * lane; j4 < T; j4 += 256)
+            *reinterpret_cast<float4 *>(srow + j4) = *reinterpret_cast<const float4 *>(&E[hl][j4]);
     }
     if (threadIdx.x < G) {
         const int hl = threadIdx.x;
@@ -106,14 +102,20 @@ __global__ __launch_bounds__(kBlock) void prop_pass1_kernel(
 // C_t (fp64, C_{n_t-1} := 1), threshold counts cnt_t = #{m : U + m/S < C_t}
 // made monotone, budgets S_t = cnt_t - cnt_{t-1}; tiles with S_t > 0 go to
 // an LDS visit list in tile order.
-// Pass 2 (one wave per visited tile): inclusive scan of the tile's stash,
-// CDF positions F_j = C_{t-1} + P_j e^{scale (m_t - M)} / Z, per-element
-// counts c_j = #{m : t_m < F_j} clamped to the tile's threshold range and
-// forced to its end from the last token of nonzero weight on, made
-// monotone; token j takes thresholds c_{j-1} .. c_j - 1 (its multiplicity
-// is c_j - c_{j-1}), written to an LDS list of selected rows.
-// Gather: the S selected rows are read (16 lanes per row, 4 rows per wave
-// instruction), summed in a fixed order and divided by S.
+// Pass 2 (LPT lanes per visited tile, EPL consecutive tokens per lane):
+// inclusive scan of the tile's stash P_j, then the count of thresholds below
+// the CDF position of token j, c_j = ceil(P_j a + b) clamped to the tile's
+// threshold range (see VisitRec).  Token j takes thresholds c_{j-1} ..
+// c_j - 1, so only the tokens where the count steps are recorded: a marker
+// (row j, multiplicity c_j - c_{j-1}) at LDS position c_{j-1}.  If the fp32
+// tile total falls short of the tile's last threshold, the remaining ones go
+// to the last token of nonzero weight, as a marker at the short count.
+// Every threshold position holds the marker of its token or lies after it
+// in the same tile, so a running max over positions gives the index list.
+// Gather: each wave reads the V rows of its own tiles' markers right away
+// (16 lanes per row, 4 rows per wave instruction) and accumulates
+// multiplicity * row; the waves' sums are added in a fixed order and
+// divided by S.
 // Visit record of a tile with S_t > 0: its thresholds are first .. first+cnt-1
 // and the number of thresholds below the CDF position of its element j is
 // ceil(P_j * a + b), with P_j the stash prefix, a = S e^{scale(m_t-M)}/Z and
@@ -125,6 +127,7 @@ struct VisitRec {
 };
 
 constexpr int kMaxTilesLds = 1024;   // tiles per request the reducer keeps in LDS
+constexpr int kGatherRounds = 4;     // V rows per lane slot in flight together in the gather
 
 // EPL consecutive floats from a 16-byte aligned address (EPL = T/64)
 template <int EPL>
@@ -143,22 +146,26 @@ __device__ __forceinline__ void load_stash(const float *p, float (&e)[EPL]) {
     }
 }
 
+// at most 64 VGPRs (8 waves per SIMD), so that two of these 1024-thread
+// workgroups share a compute unit
 template <typename KV, int T, bool PAGED>
-__global__ __launch_bounds__(kSampleBlock) void prop_sample_kernel(
+__global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8))) void prop_sample_kernel(
     const KV *__restrict__ v, KVLayout L, const int *__restrict__ seq_lens, int batch, int num_q_heads,
     int G, int S, int max_nt, int kcap, const float *__restrict__ u, float scale,
-    const float *__restrict__ stash, int stash_stride, const float2 *__restrict__ stats, float *__restrict__ out,
+    const float *__restrict__ stash, const float2 *__restrict__ stats, float *__restrict__ out,
     int *__restrict__ sample_idx, int *__restrict__ tile_budget) {
     constexpr int EPL = T / 64;
-    constexpr int NB = 4;                            // visited tiles per wave whose stash loads overlap
     extern __shared__ __align__(16) unsigned char smem[];
     VisitRec *vis = reinterpret_cast<VisitRec *>(smem);                  // [kcap]
-    int *jsel = reinterpret_cast<int *>(smem + (size_t)kcap * sizeof(VisitRec));   // [S]
+    int *jsel = reinterpret_cast<int *>(smem + (size_t)kcap * sizeof(VisitRec));   // [S] marker rows, -1 elsewhere
+    int *jmul = jsel + S;                                                  // [S] marker multiplicities
     __shared__ float red[kSampleWaves][kHeadDim];
     __shared__ float2 tstat[kMaxTilesLds];          // reducer: per-tile (m_t, Z_t)
     __shared__ double tf[kMaxTilesLds];             // reducer: e^{scale (m_t - M)}
     __shared__ double tC[kMaxTilesLds];             // reducer: tile CDF C_t
     __shared__ int nvis_sh;
+    __shared__ int wrow[kSampleWaves][kWave];        // per-wave compacted marker rows
+    __shared__ float wmul[kSampleWaves][kWave];      // and their multiplicities
 
     // block -> (request, KV head, head in group); blocks of one KV head are
     // numbered bg + i * B*Hkv, the numbering pass 1 uses for that head's tiles
@@ -180,8 +187,11 @@ __global__ __launch_bounds__(kSampleBlock) void prop_sample_kernel(
     }
     const double U = (double)u[bh];
 
-    // ---------------- reducer: wave 0, lane l owns tiles [l*CH, l*CH + CH)
-    if (w == 0) {
+    // ---------------- reducer: wave 0, lane l owns tiles [l*CH, l*CH + CH);
+    // the other waves clear the marker positions meanwhile
+    if (w != 0) {
+        for (int m = tid - kWave; m < S; m += kSampleBlock - kWave) jsel[m] = -1;
+    } else {
         const int CH = (nt + 63) / 64;
         const int tb = lane * CH, te = min(nt, tb + CH);
         const float2 *stp = stats + (size_t)bh * max_nt;
@@ -264,79 +274,126 @@ __global__ __launch_bounds__(kSampleBlock) void prop_sample_kernel(
     __syncthreads();
     const int nvis = min(nvis_sh, kcap);
 
-    // ---------------- pass 2: per visited tile, threshold counts -> jsel
-    // A wave takes TPW visited tiles at once, LPT lanes per tile, EPL
-    // consecutive stash values per lane (all loads of the wave in flight
-    // together); scans run inside each LPT-lane group.
-    {
-        constexpr int LPT = T >= 1024 ? 64 : (T >= 512 ? 32 : 16);
-        constexpr int TPW = 64 / LPT;
-        constexpr int EPL2 = T / LPT;
-        const int sub = lane / LPT, gl = lane % LPT;          // tile slot in the wave, lane in group
-        for (int k0 = w * TPW; k0 < nvis; k0 += TPW * kSampleWaves) {
-            const int kv = k0 + sub;
-            const bool active = kv < nvis;
-            const VisitRec rec = vis[active ? kv : k0];
-            const int start = rec.t * T;
-            const int len = min(T, n - start);
-            float e[EPL2];
-            // whole slice, unconditionally: stash rows are padded to a multiple
-            // of T, so the read stays inside the row; elements past the end
-            // are zeroed by the select below
-            load_stash<EPL2>(stash + (size_t)bh * stash_stride + start + gl * EPL2, e);
-            int lz = -1;
-            float run = 0.f;
-#pragma unroll
-            for (int qq = 0; qq < EPL2; ++qq) {
-                const int j = gl * EPL2 + qq;
-                const float x = (j < len) ? e[qq] : 0.f;
-                if (x > 0.f) lz = j;
-                run += x;
-                e[qq] = run;                               // in-lane inclusive prefix
-            }
-            lz = __builtin_amdgcn_ds_bpermute(4 * group_last_lane<LPT>(lane), group_incl_max<LPT>(lz));
-            const float gincl = group_incl_scan<LPT>(run);
-            float excl = __shfl_up(gincl, 1);              // sum of the earlier lanes of the group
-            if (gl == 0) excl = 0.f;
-            const int lo = rec.first, hi = rec.first + rec.cnt;
-            int cj[EPL2];
-            int lmax = lo;
-            const float flo = (float)lo, fhi = (float)hi;
-#pragma unroll
-            for (int qq = 0; qq < EPL2; ++qq) {
-                const int j = gl * EPL2 + qq;
-                const int cc = (int)fminf(fmaxf(ceilf(fmaf(excl + e[qq], rec.a, rec.b)), flo), fhi);
-                lmax = max(lmax, j < lz ? cc : hi);    // from the last nonzero weight on: all of the tile's thresholds
-                cj[qq] = lmax;                         // in-lane running max
-            }
-            const int gmax = group_incl_max<LPT>(lmax);   // running max from earlier lanes of the group
-            int pmax = __shfl_up(gmax, 1);
-            if (gl == 0) pmax = lo;
-            // thresholds pmax .. last-1 fall on this lane's elements; element
-            // qq takes those m with max(c_{qq-1}, pmax) <= m < max(c_qq, pmax)
-            const int last = active ? max(cj[EPL2 - 1], pmax) : pmax;
-            for (int m = pmax; m < last; ++m) {
-                int q = 0;
-#pragma unroll
-                for (int qq = 0; qq < EPL2; ++qq) q += (cj[qq] <= m) ? 1 : 0;
-                jsel[m] = start + gl * EPL2 + q;
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---------------- gather the S selected rows
-    const int slot = lane >> 4, chunk = lane & 15;
+    // ---------------- pass 2 + gather, per wave: TPW visited tiles at once,
+    // LPT lanes per tile, EPL2 consecutive stash values per lane
+    constexpr int LPT = T >= 1024 ? 64 : (T >= 512 ? 32 : 16);
+    constexpr int TPW = 64 / LPT;
+    constexpr int EPL2 = T / LPT;
+    const int sub = lane / LPT, gl = lane % LPT;          // tile slot in the wave, lane in group
+    const int slot = lane >> 4, chunk = lane & 15;        // gather: row slot, 8-element chunk
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll 4
-    for (int m = 4 * w + slot; m < S; m += 4 * kSampleWaves) {
-        const int row = jsel[m];
-        float xv[8];
-        load_v8<KV>(v + row_offset(L, b, g, row) + 8 * chunk, xv);
+    for (int k0 = w * TPW; k0 < nvis; k0 += TPW * kSampleWaves) {
+        const int kv = k0 + sub;
+        const bool active = kv < nvis;
+        const VisitRec rec = vis[active ? kv : k0];
+        const int start = rec.t * T;
+        float e[EPL2];
+        // whole slice, unconditionally: pass 1 writes every tile in full,
+        // with 0 past the sequence end
+        load_stash<EPL2>(stash + (size_t)bh * max_nt * T + start + gl * EPL2, e);
+        float run = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += xv[e];
+        for (int qq = 0; qq < EPL2; ++qq) {
+            run += e[qq];
+            e[qq] = run;                                   // in-lane inclusive prefix
+        }
+        const float gincl = group_incl_scan<LPT>(run);
+        float excl = __shfl_up(gincl, 1);                  // sum of the earlier lanes of the group
+        if (gl == 0) excl = 0.f;
+        // x_j = P_j a + b for the lane's tokens: e_j a + (excl a + b), monotone
+        // in the lane; across lanes a running max keeps the counts monotone
+        const float bl = fmaf(excl, rec.a, rec.b);
+        const int lo = rec.first, hi = rec.first + rec.cnt;
+        const float fhi = (float)hi;
+        const int yl = max((int)fminf(ceilf(fmaf(e[EPL2 - 1], rec.a, bl)), fhi), lo);
+        const int gmax = group_incl_max<LPT>(yl);
+        int prev = __shfl_up(gmax, 1);                     // count reached by the earlier lanes
+        if (gl == 0) prev = lo;
+        if (active && yl > prev) {                         // thresholds prev .. yl-1 fall on this lane
+            int yp = prev;
+#pragma unroll
+            for (int qq = 0; qq < EPL2; ++qq) {
+                const int y = (int)fminf(ceilf(fmaf(e[qq], rec.a, bl)), fhi);
+                if (y > yp) {
+                    // a step can fall on a token of zero weight only through
+                    // fp32 rounding across lanes (a threshold within ~1e-7 of
+                    // that token's CDF position); past the sequence end such
+                    // a token is replaced by the last one, so every row read
+                    // is inside the request
+                    jsel[yp] = min(start + gl * EPL2 + qq, n - 1);
+                    jmul[yp] = y - yp;
+                    yp = y;
+                }
+            }
+        }
+        const int yend = __builtin_amdgcn_ds_bpermute(4 * group_last_lane<LPT>(lane), gmax);
+        if (active && yend < hi) {
+            // rare: the fp32 tile total is short of the tile's last threshold;
+            // thresholds yend .. hi-1 go to the last token whose weight moved P
+            int lz = -1;
+#pragma unroll
+            for (int qq = 0; qq < EPL2; ++qq)
+                if (e[qq] > (qq ? e[qq - 1] : 0.f)) lz = gl * EPL2 + qq;
+            lz = group_incl_max<LPT>(lz);
+            if (gl == LPT - 1) {
+                jsel[yend] = start + max(lz, 0);
+                jmul[yend] = hi - yend;
+            }
+        }
+        // the wave's threshold range [m0, m1): from its first tile's first
+        // threshold to its last active tile's end
+        const int m0 = __shfl(lo, 0);
+        const int m1 = wave_max(active ? hi : 0);
+        wave_sync_lds();
+        if (sample_idx) {
+            // each position takes the row of the nearest marker at or before
+            // it (a running max over marker positions; m0 always holds one)
+            int carry = m0;
+            for (int c = m0; c < m1; c += kWave) {
+                const int m = c + lane;
+                int pm = (m < m1 && jsel[m] >= 0) ? m : -1;
+                pm = max(wave_incl_max_scan(pm, lane), carry);
+                if (m < m1) sample_idx[(size_t)bh * S + m] = jsel[pm];
+                carry = __builtin_amdgcn_readlane(pm, 63);
+            }
+        }
+        // gather: the markers of [m0, m1), 64 positions at a time, are
+        // compacted into the wave's LDS list, then read 4 rows per wave
+        // instruction with every load of a round in flight together
+        for (int c = m0; c < m1; c += kWave) {
+            const int m = c + lane;
+            const int r = (m < m1) ? jsel[m] : -1;
+            const unsigned long long bal = __ballot(r >= 0);
+            const int nm = __popcll(bal);
+            if (r >= 0) {
+                const int pos = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+                wrow[w][pos] = r;
+                wmul[w][pos] = (float)jmul[m];
+            }
+            wave_sync_lds();
+            for (int i0 = 0; i0 < nm; i0 += 4 * kGatherRounds) {
+                int rows[kGatherRounds];
+                float mul[kGatherRounds];
+#pragma unroll
+                for (int u = 0; u < kGatherRounds; ++u) {
+                    // slots past the list re-read its first row with weight 0
+                    const int idx = i0 + slot + 4 * u;
+                    rows[u] = wrow[w][idx < nm ? idx : 0];
+                    mul[u] = idx < nm ? wmul[w][idx] : 0.f;
+                }
+                float xv[kGatherRounds][8];
+#pragma unroll
+                for (int u = 0; u < kGatherRounds; ++u) load_v8<KV>(v + row_offset(L, b, g, rows[u]) + 8 * chunk, xv[u]);
+#pragma unroll
+                for (int u = 0; u < kGatherRounds; ++u)
+#pragma unroll
+                    for (int e2 = 0; e2 < 8; ++e2) acc[e2] = fmaf(mul[u], xv[u][e2], acc[e2]);
+            }
+            wave_sync_lds();
+        }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -347,8 +404,6 @@ __global__ __launch_bounds__(kSampleBlock) void prop_sample_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) red[w][8 * chunk + e] = acc[e];
     }
-    if (sample_idx)
-        for (int m = tid; m < S; m += kSampleBlock) sample_idx[(size_t)bh * S + m] = jsel[m];
     __syncthreads();
     if (tid < kHeadDim) {
         float sum = 0.f;
@@ -364,7 +419,7 @@ __global__ __launch_bounds__(kSampleBlock) void prop_sample_kernel(
 // launchers
 // ===================================================================
 size_t prop_sample_lds_bytes(int kcap, int S) {
-    return (size_t)kcap * sizeof(VisitRec) + (size_t)S * sizeof(int);
+    return (size_t)kcap * sizeof(VisitRec) + 2 * (size_t)S * sizeof(int);
 }
 
 template <typename KV, int G, int T, bool PAGED>
@@ -379,18 +434,18 @@ static hipError_t launch_prop_t(const LaunchArgs &a, const TimingHook &hook) {
     if (hook.begin)
         hipExtLaunchKernelGGL((prop_pass1_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * max_nt)), dim3(kBlock), 0, st, (hipEvent_t)hook.begin, (hipEvent_t)hook.end, 0,
                        (const KV *)a.q, (const KV *)a.k, L, a.seq_lens, a.num_q_heads, max_nt, a.scale,
-                       stash, a.stash_stride, stats);
+                       stash, stats);
     else
         hipLaunchKernelGGL((prop_pass1_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * max_nt)), dim3(kBlock), 0, st,
                        (const KV *)a.q, (const KV *)a.k, L, a.seq_lens, a.num_q_heads, max_nt, a.scale,
-                       stash, a.stash_stride, stats);
+                       stash, stats);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int BH = a.batch * a.num_q_heads;
     hipLaunchKernelGGL((prop_sample_kernel<KV, T, PAGED>), dim3((unsigned)BH), dim3(kSampleBlock),
                        prop_sample_lds_bytes(a.kmax, a.S), st, (const KV *)a.v, L, a.seq_lens, a.batch,
                        a.num_q_heads, G, a.S, max_nt, a.kmax, a.u, a.scale, (const float *)stash,
-                       a.stash_stride, (const float2 *)stats, a.out, a.sample_idx, a.tile_budget);
+                       (const float2 *)stats, a.out, a.sample_idx, a.tile_budget);
     return hipGetLastError();
 }
 
