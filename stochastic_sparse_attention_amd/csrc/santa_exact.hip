@@ -40,14 +40,19 @@ __global__ __launch_bounds__(kBlock) void exact_partial_kernel(
     if (t0 >= n) return;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 
-    SC sc;
-    sc.load_q(q + ((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim);
-    sc.score(k, L, b, g, t0, n);
-
+    // LDS: the scorer's staging area, then (after the barrier in tile_max)
+    // the tile's weights Pw[G][T] and the per-wave V sums red_o
+    constexpr int kPwBytes = G * T * 4, kRedBytes = kWavesPerBlock * G * kHeadDim * 4;
+    __shared__ __align__(16) unsigned char lds[cmax(SC::kStageVec * 16, kPwBytes + kRedBytes)];
     __shared__ float red_m[kWavesPerBlock][16];
     __shared__ float red_l[kWavesPerBlock][16];
-    __shared__ float Pw[G][T];
-    __shared__ float red_o[kWavesPerBlock][G][kHeadDim];
+    float (*Pw)[T] = reinterpret_cast<float (*)[T]>(lds);
+    float (*red_o)[G][kHeadDim] = reinterpret_cast<float (*)[G][kHeadDim]>(lds + kPwBytes);
+
+    SC sc;
+    sc.load_q(q + ((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim);
+    sc.score(k, L, b, g, t0, n, reinterpret_cast<u32x4 *>(lds));
+
     float mt[SC::NV];
     tile_max(sc, red_m, mt);
     const acc_t c2 = (acc_t)scale * (acc_t)1.4426950408889634;

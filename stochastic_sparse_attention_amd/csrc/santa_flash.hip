@@ -50,12 +50,16 @@ __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
     const int t0 = tile * T;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 
+    // LDS: the scorer's staging area, then (after the barrier in tile_max)
+    // the tile's exp-weights E[G][T]
+    __shared__ __align__(16) unsigned char lds[cmax(SC::kStageVec * 16, G * T * 4)];
+    __shared__ float red_m[kWavesPerBlock][16];
+    float (*E)[T] = reinterpret_cast<float (*)[T]>(lds);
+
     SC sc;
     sc.load_q(q + ((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim);
-    sc.score(k, L, b, g, t0, n);
+    sc.score(k, L, b, g, t0, n, reinterpret_cast<u32x4 *>(lds));
 
-    __shared__ float red_m[kWavesPerBlock][16];
-    __shared__ float E[G][T];
     float mt[SC::NV];
     tile_max(sc, red_m, mt);
     const acc_t c2 = (acc_t)scale * (acc_t)1.4426950408889634;

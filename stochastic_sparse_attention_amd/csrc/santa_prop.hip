@@ -43,13 +43,17 @@ __global__ __launch_bounds__(kBlock) void prop_pass1_kernel(
     if (t0 >= n) return;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 
-    SC sc;
-    sc.load_q(q + ((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim);
-    sc.score(k, L, b, g, t0, n);
-
+    // LDS: the scorer's staging area, then (after the barrier in tile_max)
+    // the tile's stash rows E[G][T], staged for wide stores
+    __shared__ __align__(16) unsigned char lds[cmax(SC::kStageVec * 16, G * T * 4)];
     __shared__ float red_m[kWavesPerBlock][16];
     __shared__ float red_z[kWavesPerBlock][16];
-    __shared__ __align__(16) float E[G][T];           // the tile's stash rows, staged for wide stores
+    float (*E)[T] = reinterpret_cast<float (*)[T]>(lds);
+
+    SC sc;
+    sc.load_q(q + ((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim);
+    sc.score(k, L, b, g, t0, n, reinterpret_cast<u32x4 *>(lds));
+
     float mt[SC::NV];
     tile_max(sc, red_m, mt);
 

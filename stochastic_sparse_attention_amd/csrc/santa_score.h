@@ -8,9 +8,9 @@
 //  * MFMA (bf16 K): the group's queries are the A operand of
 //    v_mfma_f32_16x16x32_bf16 (16 rows = heads, padded with zeros), 16 K rows
 //    are the B operand (16 columns = tokens), 4 MFMAs cover d = 128.  Lane l
-//    loads 16 bytes of token l%16 at d = 32 kb + 8 (l/16) for kb = 0..3 and
+//    takes 16 bytes of token l%16 at d = 32 kb + 8 (l/16) for kb = 0..3 and
 //    receives the scores of heads 4 (l/16) + v, v = 0..3, for that token.
-//    Each token's 256-byte row is read as four 64-byte pieces per MFMA step.
+//    K is loaded as whole 256-byte rows and transposed through LDS.
 //  * VALU (fp32 K, fp64 accumulation; also bf16 when SANTA_BF16_VALU is
 //    defined, for comparison): 4 lanes per row, each holding 16-byte chunks
 //    c, c+4, ... of the row; partial dots for every head, a quad sum, then
@@ -64,7 +64,8 @@ struct ScorerMfma {
     typedef float acc_t;
     static constexpr int NS = T / 64;
     static constexpr int NV = 4;
-    static constexpr int CH = NS < 4 ? NS : 4;   // steps whose K loads are in flight together
+    static constexpr int CH = NS < 2 ? NS : 2;   // steps whose K loads are in flight together
+    static constexpr int kStageVec = kWavesPerBlock * 256;   // LDS staging, 16-byte units (4 KiB per wave)
     bf16x8_t qa[4];
     acc_t x[NS][NV];
 
@@ -86,10 +87,17 @@ struct ScorerMfma {
                 bf16x8_t, *reinterpret_cast<const u32x4 *>(q_group + hsrc * kHeadDim + 32 * kb + 8 * kq));
     }
 
+    // K is read 4 whole rows (4 x 256 bytes) per load instruction: lane l
+    // holds 16-byte piece l%16 of row 4 kb + l/16 of the wave's 16-row block.
+    // The block then goes through the wave's 4 KiB of `stage` (piece p of row
+    // r at slot p ^ r, so that both the row-wise writes and the token-wise
+    // reads touch every bank once) into the MFMA layout: lane l reads piece
+    // 4 kb + l/16 of token l%16.
     __device__ __forceinline__ void score(const uint16_t *__restrict__ k, const KVLayout &L, int b, int g,
-                                          int t0, int n) {
+                                          int t0, int n, u32x4 *stage) {
         const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
         const int tok = lane & 15, kq = lane >> 4;
+        u32x4 *wst = stage + w * 256;
 #pragma unroll
         for (int s0 = 0; s0 < NS; s0 += CH) {
             size_t base[CH];
@@ -98,21 +106,32 @@ struct ScorerMfma {
             u32x4 kv[CH][4];
 #pragma unroll
             for (int ii = 0; ii < CH; ++ii) {
-                // rows past the end read the block's row 0 (always a valid row
-                // of the tile); their scores are masked below
-                const bool valid = t0 + 64 * (s0 + ii) + 16 * w + tok < n;
-                const u32x4 *rowp =
-                    reinterpret_cast<const u32x4 *>(k + base[ii] + (size_t)(valid ? tok : 0) * kHeadDim) + kq;
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) kv[ii][kb] = __builtin_nontemporal_load(rowp + 4 * kb);
+                for (int kb = 0; kb < 4; ++kb) {
+                    // rows past the end read the block's row 0 (always a valid
+                    // row of the tile); their scores are masked below
+                    const int r = 4 * kb + kq;
+                    const bool valid = t0 + 64 * (s0 + ii) + 16 * w + r < n;
+                    const u32x4 *rowp =
+                        reinterpret_cast<const u32x4 *>(k + base[ii] + (size_t)(valid ? r : 0) * kHeadDim) + tok;
+                    kv[ii][kb] = __builtin_nontemporal_load(rowp);
+                }
             }
 #pragma unroll
             for (int ii = 0; ii < CH; ++ii) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const int r = 4 * kb + kq;
+                    wst[r * 16 + (tok ^ r)] = kv[ii][kb];
+                }
+                wave_sync_lds();
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], __builtin_bit_cast(bf16x8_t, kv[ii][kb]),
-                                                                  acc, 0, 0, 0);
+                for (int kb = 0; kb < 4; ++kb) {
+                    const u32x4 kt = wst[tok * 16 + ((4 * kb + kq) ^ tok)];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], __builtin_bit_cast(bf16x8_t, kt), acc, 0, 0, 0);
+                }
+                wave_sync_lds();
                 const bool valid = t0 + 64 * (s0 + ii) + 16 * w + tok < n;
 #pragma unroll
                 for (int v = 0; v < NV; ++v)
@@ -143,6 +162,7 @@ struct ScorerValu {
     static constexpr int CHMAX = G <= 2 ? 4 : 2;
     static constexpr int CH = NS < CHMAX ? NS : CHMAX;
     static constexpr int ROW_VEC = kHeadDim * (int)sizeof(KV) / 16;
+    static constexpr int kStageVec = 0;                       // no LDS staging
     u32x4 qv[G][NC];
     acc_t x[NS][NV];
 
@@ -162,7 +182,7 @@ struct ScorerValu {
     }
 
     __device__ __forceinline__ void score(const KV *__restrict__ k, const KVLayout &L, int b, int g, int t0,
-                                          int n) {
+                                          int n, u32x4 * /*stage: unused*/) {
         const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
         const int c = lane & 3, r = lane >> 2;
 #pragma unroll
@@ -216,6 +236,8 @@ template <int G, int T, bool PAGED> struct ScorerFor<uint16_t, G, T, PAGED> {
     typedef ScorerMfma<G, T, PAGED> type;
 };
 #endif
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // Per-head tile maximum of the unscaled scores: red_m[w][head] holds each
 // wave's maximum, mt[v] the tile maximum of this lane's v-th head.
