@@ -74,27 +74,46 @@ __global__ __launch_bounds__(kBlock) void exact_partial_kernel(
     }
     __syncthreads();
 
-    // V pass: 16 lanes per row (8 elements each), 4 rows per wave step,
-    // 16 consecutive rows per block step
+    // V pass: wave w takes the 16-row blocks 64 s + 16 w of the tile (as the
+    // scorer does), 16 lanes per row (8 elements each), 4 rows per load
+    // instruction; the loads of VCH blocks are in flight together and rows
+    // past the end read the block's row 0 with weight 0 (Pw is 0 there)
+    constexpr int NSV = T / 64;
+    constexpr int VCH = NSV < 2 ? NSV : 2;
     const int slot = lane >> 4, chunk = lane & 15;
     float acc[G][8];
 #pragma unroll
     for (int hl = 0; hl < G; ++hl)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[hl][e] = 0.f;
-#pragma unroll 4
-    for (int i2 = 0; i2 < T / 16; ++i2) {
-        const int row = 16 * i2 + 4 * w + slot;
-        if (t0 + row < n) {
-            float xv[8];
-            load_v8<KV>(v + row_offset(L, b, g, t0 + row) + 8 * chunk, xv);
 #pragma unroll
-            for (int hl = 0; hl < G; ++hl) {
-                const float p = Pw[hl][row];
+    for (int s0 = 0; s0 < NSV; s0 += VCH) {
+        Raw8<KV> vv[VCH][4];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[hl][e] = fmaf(p, xv[e], acc[hl][e]);
+        for (int ii = 0; ii < VCH; ++ii) {
+            const int j0 = t0 + 64 * (s0 + ii) + 16 * w;
+            const size_t vb = block_base<PAGED>(L, b, g, j0, n, t0);
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int r = 4 * r4 + slot;
+                const bool valid = j0 + r < n;
+                vv[ii][r4] = load_raw8<KV>(v + vb + (size_t)(valid ? r : 0) * kHeadDim + 8 * chunk);
             }
         }
+#pragma unroll
+        for (int ii = 0; ii < VCH; ++ii)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int row = 64 * (s0 + ii) + 16 * w + 4 * r4 + slot;
+                float xv[8];
+                widen8(vv[ii][r4], xv);
+#pragma unroll
+                for (int hl = 0; hl < G; ++hl) {
+                    const float p = Pw[hl][row];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[hl][e] = fmaf(p, xv[e], acc[hl][e]);
+                }
+            }
     }
 #pragma unroll
     for (int hl = 0; hl < G; ++hl)

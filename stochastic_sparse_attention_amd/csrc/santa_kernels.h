@@ -135,6 +135,33 @@ __device__ __forceinline__ void load_v8<float>(const float *p, float (&v)[8]) {
     v[6] = __uint_as_float(c.z); v[7] = __uint_as_float(c.w);
 }
 
+// 8 consecutive elements of a V row kept in storage form (so that many
+// loads can be in flight in few registers), widened to fp32 at use
+template <typename KV> struct Raw8;
+template <> struct Raw8<uint16_t> { u32x4 x[1]; };
+template <> struct Raw8<float> { u32x4 x[2]; };
+
+template <typename KV>
+__device__ __forceinline__ Raw8<KV> load_raw8(const KV *p) {
+    Raw8<KV> r;
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(r.x) / sizeof(u32x4)); ++i) r.x[i] = reinterpret_cast<const u32x4 *>(p)[i];
+    return r;
+}
+__device__ __forceinline__ void widen8(const Raw8<uint16_t> &r, float (&v)[8]) {
+    const u32x4 a = r.x[0];
+    v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x);
+    v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+    v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z);
+    v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+}
+__device__ __forceinline__ void widen8(const Raw8<float> &r, float (&v)[8]) {
+    v[0] = __uint_as_float(r.x[0].x); v[1] = __uint_as_float(r.x[0].y);
+    v[2] = __uint_as_float(r.x[0].z); v[3] = __uint_as_float(r.x[0].w);
+    v[4] = __uint_as_float(r.x[1].x); v[5] = __uint_as_float(r.x[1].y);
+    v[6] = __uint_as_float(r.x[1].z); v[7] = __uint_as_float(r.x[1].w);
+}
+
 // ===================================================================
 // Merge of per-tile (m_t, l_t, o_t): out = sum_t w_t o_t / norm with
 // w_t = e^{scale (m_t - M)} * coef_t.  Flash: coef_t = Z_t (the tile's true
