@@ -145,6 +145,8 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-exact", action="store_true")
+    ap.add_argument("--no-flash", action="store_true",
+                    help="skip the S2ANTA-flash leg (run where the workload has a flash budget)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 device copies of 256 MiB (known traffic: 256 MiB read and "
                          "256 MiB written each) to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -269,6 +271,34 @@ def main(argv=None):
             "partial_kernel_GB/s": round(eb["partial"] / (np.mean(ekern) * 1e-3) / 1e9, 1),
         }
         result["speedup_vs_exact"] = round(ems / ms, 3)
+
+    if cfg.S_flash and not args.no_flash:
+        Sf = cfg.S_flash
+        wsf = torch.empty(sa.santa_workspace_size(dev.problem, "flash", Sf), dtype=torch.uint8, device=dev0)
+        outf = torch.empty_like(out)
+        uf = dev.u(Sf)
+
+        def flash_step(i):
+            c = i % ncopy
+            sa.santa_decode_flash(dev.problem, dev.q, ks[c], vs[c], Sf, uf, outf, workspace=wsf)
+
+        fms_eager, fkern = time_steps(flash_step, args.steps, args.warmup, events=True)
+        fms = fms_eager
+        if args.mode == "graph":
+            fms, _gf = time_graph(flash_step, ncopy, args.steps, args.warmup)
+        fb = BM.flash_step_bytes(cfg, Sf, T)
+        log(f"bench: flash S={Sf} {fms * 1e3:.2f} us/step (eager {fms_eager * 1e3:.2f}), "
+            f"tile kernel {np.mean(fkern) * 1e3:.2f} us")
+        result["santa_flash"] = {
+            "S": Sf,
+            "us_per_step": round(fms * 1e3, 3),
+            "eager_us_per_step": round(fms_eager * 1e3, 3),
+            "GB/s": round(fb["total"] / (fms * 1e-3) / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * fb["total"] / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "tile_kernel_us": round(float(np.mean(fkern)) * 1e3, 3),
+            "tile_kernel_GB/s": round(fb["tile"] / (np.mean(fkern) * 1e-3) / 1e9, 1),
+            "prop_speedup_vs_flash": round(fms / ms, 3),
+        }
 
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
