@@ -115,24 +115,78 @@ def time_graph(step_fn, ncopy, steps, warmup):
         g.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    return (t1 - t0) * 1e3 / (reps * ncopy), g
+    # a second pass with events around each replay gives the spread
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) / ncopy for a, b in evs])
+    spread = {q: round(float(np.percentile(per, q)) * 1e3, 3) for q in (10, 50, 90)}
+    return (t1 - t0) * 1e3 / (reps * ncopy), spread
 
 
-def cpu_baseline(inp, S, seconds):
-    """The fp64 oracle on the host cores (a reported baseline, not the target)."""
-    import oracle as O
-    prob = O.Problem.from_inputs(inp)
-    u = inp.u(S)
+def copy_peak_gbs(torch, dev, nbytes=512 << 20, reps=10):
+    """Device-to-device copy rate (read + write bytes per second), the
+    measured ceiling beside the 8 TB/s spec."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del a, b
+    return 2 * nbytes / sec / 1e9
+
+
+def _median_time(fn, seconds, max_reps=50):
     reps, secs = 0, []
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        O.santa_prop(prob, inp.q, inp.k, inp.v, S, u)
+        fn()
         secs.append(time.perf_counter() - t0)
         reps += 1
-        if time.perf_counter() - t_start >= seconds or reps >= 50:
+        if time.perf_counter() - t_start >= seconds or reps >= max_reps:
             break
-    return float(np.median(secs)), reps, O.num_threads()
+    return float(np.median(secs)), reps
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inp, S, seconds):
+    """The fp64 oracle on the host cores (a reported baseline, not the target):
+    prop with OpenMP over the heads at the default thread count, prop on one
+    thread, and the exact decode at the default thread count."""
+    import oracle as O
+    prob = O.Problem.from_inputs(inp)
+    u = inp.u(S)
+    cores = O.num_threads()
+    prop_s, reps = _median_time(lambda: O.santa_prop(prob, inp.q, inp.k, inp.v, S, u), seconds)
+    exact_s, ereps = _median_time(lambda: O.exact(prob, inp.q, inp.k, inp.v), seconds / 4, 10)
+    O.set_num_threads(1)
+    try:
+        single_s, sreps = _median_time(lambda: O.santa_prop(prob, inp.q, inp.k, inp.v, S, u), seconds / 2, 5)
+    finally:
+        O.set_num_threads(cores)
+    return {"prop_s": prop_s, "reps": reps, "cores": cores, "exact_s": exact_s, "exact_reps": ereps,
+            "single_s": single_s, "single_reps": sreps}
 
 
 def main(argv=None):
@@ -199,9 +253,10 @@ def main(argv=None):
     ms_eager, kern = time_steps(prop_step, args.steps, args.warmup, events=True)
     log(f"bench: prop eager {ms_eager * 1e3:.2f} us/step, pass-1 {np.mean(kern) * 1e3:.2f} us")
     ms = ms_eager
+    spread = None
     if args.mode == "graph":
-        ms, _g = time_graph(prop_step, ncopy, args.steps, args.warmup)
-        log(f"bench: prop graph {ms * 1e3:.2f} us/step")
+        ms, spread = time_graph(prop_step, ncopy, args.steps, args.warmup)
+        log(f"bench: prop graph {ms * 1e3:.2f} us/step (p10/p50/p90 {spread})")
 
     # one more call with the optional outputs, for the byte count and V-row share
     max_nt = (cfg.seq_len + T - 1) // T
@@ -216,6 +271,10 @@ def main(argv=None):
     kern_ms = float(np.mean(kern))
     achieved = pass1_bytes / (kern_ms * 1e-3) / 1e9
     step_gbs = nbytes["total"] / (ms * 1e-3) / 1e9
+
+    copy_gbs = copy_peak_gbs(torch, dev0)
+    log(f"bench: device copy peak {copy_gbs:.1f} GB/s (read + write bytes)")
+    kern_sorted = np.sort(np.array(kern))
 
     result = {
         "metric": METRIC,
@@ -238,13 +297,19 @@ def main(argv=None):
         "timing_mode": args.mode,
         "eager_us_per_step": round(ms_eager * 1e3, 3),
         "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
+        "step_us_p10_p50_p90": spread,
+        "copy_peak_GB/s": round(copy_gbs, 1),
+        "pct_of_copy_peak": round(100 * step_gbs / copy_gbs, 2),
         "algorithmic_bytes_per_step": nbytes,
         "v_row_fraction": round(BM.v_row_fraction(idx_np, cfg, seq), 6),
         "tiles_visited_per_head": round(float((tb_np > 0).sum(1).mean()), 2),
         "roofline": {"kernel": "prop_pass1_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": read_traffic("prop_pass1_kernel"),
-                     "bytes_per_launch": pass1_bytes, "avg_launch_us": round(kern_ms * 1e3, 3)},
+                     "bytes_per_launch": pass1_bytes, "avg_launch_us": round(kern_ms * 1e3, 3),
+                     "launch_us_p10_p50_p90": [round(float(np.percentile(kern_sorted, q)) * 1e3, 3)
+                                               for q in (10, 50, 90)],
+                     "frac_of_copy_peak": round(achieved / copy_gbs, 4)},
     }
 
     if not args.no_exact:
@@ -258,7 +323,7 @@ def main(argv=None):
         ems_eager, ekern = time_steps(exact_step, args.steps, args.warmup, events=True)
         ems = ems_eager
         if args.mode == "graph":
-            ems, _ge = time_graph(exact_step, ncopy, args.steps, args.warmup)
+            ems, _espread = time_graph(exact_step, ncopy, args.steps, args.warmup)
         eb = BM.exact_step_bytes(cfg, T, seq)
         log(f"bench: exact {ems * 1e3:.2f} us/step (eager {ems_eager * 1e3:.2f}), "
             f"partial {np.mean(ekern) * 1e3:.2f} us")
@@ -285,7 +350,7 @@ def main(argv=None):
         fms_eager, fkern = time_steps(flash_step, args.steps, args.warmup, events=True)
         fms = fms_eager
         if args.mode == "graph":
-            fms, _gf = time_graph(flash_step, ncopy, args.steps, args.warmup)
+            fms, _fspread = time_graph(flash_step, ncopy, args.steps, args.warmup)
         fb = BM.flash_step_bytes(cfg, Sf, T)
         log(f"bench: flash S={Sf} {fms * 1e3:.2f} us/step (eager {fms_eager * 1e3:.2f}), "
             f"tile kernel {np.mean(fkern) * 1e3:.2f} us")
@@ -302,11 +367,15 @@ def main(argv=None):
 
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
-        sec, reps, cores = cpu_baseline(inp, S, args.cpu_seconds)
+        cb = cpu_baseline(inp, S, args.cpu_seconds)
+        sec = cb["prop_s"]
         result["cpu_baseline"] = {
-            "value": round(nbytes["total"] / sec / 1e9, 3), "unit": "GB/s", "cores": cores,
+            "value": round(nbytes["total"] / sec / 1e9, 3), "unit": "GB/s", "cores": cb["cores"],
             "kind": "oracle", "us_per_step": round(sec * 1e6, 1),
-            "sample": f"{reps} full steps of the same workload (all {BH} heads), median",
+            "sample": f"{cb['reps']} full steps of the same workload (all {BH} heads), median",
+            "single_thread_us_per_step": round(cb["single_s"] * 1e6, 1),
+            "exact_us_per_step": round(cb["exact_s"] * 1e6, 1),
+            "cpu_model": cpu_model(),
         }
     print(json.dumps(result), flush=True)
     return 0
