@@ -150,6 +150,104 @@ __device__ __forceinline__ void load_stash(const float *p, float (&e)[EPL]) {
     }
 }
 
+// Reducer of one head on one wave, with each lane's tiles (at most CHR of
+// them: lane l owns tiles [l*CH, l*CH + CH), CH = ceil(n_t/64)) held in
+// registers.  Writes the visit list, its length and the optional budgets.
+// The arithmetic and its order are those of the LDS variant in the kernel.
+template <int CHR>
+__device__ __forceinline__ void reduce_in_registers(const float2 *__restrict__ stp, int nt, int lane, double U,
+                                                    int S, float scale, int kcap, VisitRec *vis,
+                                                    int *__restrict__ budget, int max_nt, int &nvis_out) {
+    const int CH = (nt + 63) / 64;
+    const int tb = lane * CH;
+    float2 st[CHR];
+    float lmaxv = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < CHR; ++i) {
+        const bool ok = i < CH && tb + i < nt;
+        st[i] = ok ? stp[tb + i] : make_float2(-INFINITY, 0.f);
+        lmaxv = fmaxf(lmaxv, st[i].x);
+    }
+    const float Mf = wave_max(lmaxv);
+    // tile weight e^{scale (m_t - M)} in fp32 (see the LDS variant)
+    const float c2 = scale * 1.4426950408889634f;
+    double f[CHR];
+    double lsum = 0.0;
+#pragma unroll
+    for (int i = 0; i < CHR; ++i) {
+        const bool ok = i < CH && tb + i < nt;
+        f[i] = ok ? (double)exp2f((st[i].x - Mf) * c2) : 0.0;
+        if (ok) lsum += (double)st[i].y * f[i];
+    }
+    const double incl = wave_incl_scan(lsum, lane);
+    double excl = __shfl_up(incl, 1);
+    if (lane == 0) excl = 0.0;
+    const double Z = __shfl(incl, 63);
+    const double invZ = 1.0 / Z;
+    double C[CHR];
+    int c[CHR];
+    double lrun = 0.0, clast = 0.0;
+    int lcnt = 0;
+#pragma unroll
+    for (int i = 0; i < CHR; ++i) {
+        const bool ok = i < CH && tb + i < nt;
+        if (ok) lrun += (double)st[i].y * f[i];
+        C[i] = (tb + i == nt - 1) ? 1.0 : (excl + lrun) * invZ;
+        c[i] = thresholds_below(C[i], U, S);
+        if (ok) {
+            lcnt = max(lcnt, c[i]);
+            clast = C[i];
+        }
+    }
+    const int cmax = wave_incl_max_scan(lcnt, lane);
+    int cpred = __shfl_up(cmax, 1);
+    double Cpred = __shfl_up(clast, 1);      // C of the previous lane's last tile
+    if (lane == 0) {
+        cpred = 0;
+        Cpred = 0.0;
+    }
+    int nvl = 0;
+    {
+        int cp = cpred;
+#pragma unroll
+        for (int i = 0; i < CHR; ++i) {
+            if (i < CH && tb + i < nt) {
+                const int cnt = max(cp, c[i]);
+                nvl += cnt > cp;
+                cp = cnt;
+            }
+        }
+    }
+    const int vincl = wave_incl_scan(nvl, lane);
+    int vpos = vincl - nvl;
+    if (lane == 63) nvis_out = vincl;
+    int cp = cpred;
+    double cprev = Cpred;
+#pragma unroll
+    for (int i = 0; i < CHR; ++i) {
+        const int t = tb + i;
+        if (i < CH && t < nt) {
+            const int cnt = max(cp, c[i]);
+            const int St = cnt - cp;
+            if (budget) budget[t] = St;
+            if (St > 0 && vpos < kcap) {
+                VisitRec rec;
+                rec.t = t;
+                rec.first = cp;
+                rec.cnt = St;
+                rec.a = (float)((double)S * f[i] * invZ);
+                rec.b = (float)((double)S * (cprev - U));
+                vis[vpos] = rec;
+                ++vpos;
+            }
+            cp = cnt;
+            cprev = C[i];
+        }
+    }
+    if (budget)
+        for (int t = nt + lane; t < max_nt; t += 64) budget[t] = 0;
+}
+
 // at most 64 VGPRs (8 waves per SIMD), so that two of these 1024-thread
 // workgroups share a compute unit
 template <typename KV, int T, bool PAGED>
@@ -167,6 +265,7 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
     __shared__ float2 tstat[kMaxTilesLds];          // reducer: per-tile (m_t, Z_t)
     __shared__ double tf[kMaxTilesLds];             // reducer: e^{scale (m_t - M)}
     __shared__ double tC[kMaxTilesLds];             // reducer: tile CDF C_t
+    __shared__ int tcn[kMaxTilesLds];               // reducer: thresholds below C_t
     __shared__ int nvis_sh;
     __shared__ int wrow[kSampleWaves][kWave];        // per-wave compacted marker rows
     __shared__ float wmul[kSampleWaves][kWave];      // and their multiplicities
@@ -195,7 +294,17 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
     // the other waves clear the marker positions meanwhile
     if (w != 0) {
         for (int m = tid - kWave; m < S; m += kSampleBlock - kWave) jsel[m] = -1;
+    } else if (nt <= 256) {
+        const float2 *stp = stats + (size_t)bh * max_nt;
+        int *budget = tile_budget ? tile_budget + (size_t)bh * max_nt : nullptr;
+        if (nt <= 64)
+            reduce_in_registers<1>(stp, nt, lane, U, S, scale, kcap, vis, budget, max_nt, nvis_sh);
+        else if (nt <= 128)
+            reduce_in_registers<2>(stp, nt, lane, U, S, scale, kcap, vis, budget, max_nt, nvis_sh);
+        else
+            reduce_in_registers<4>(stp, nt, lane, U, S, scale, kcap, vis, budget, max_nt, nvis_sh);
     } else {
+        // more than 4 tiles per lane: per-tile values staged in LDS
         const int CH = (nt + 63) / 64;
         const int tb = lane * CH, te = min(nt, tb + CH);
         const float2 *stp = stats + (size_t)bh * max_nt;
@@ -221,15 +330,19 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
         double excl = __shfl_up(incl, 1);
         if (lane == 0) excl = 0.0;
         const double Z = __shfl(incl, 63);
-        // C_t = (excl + lane-local running sum) / Z, C_{n_t-1} := 1; counts
-        // of thresholds below each C_t, made monotone across lanes
+        const double invZ = 1.0 / Z;
+        // C_t = (excl + lane-local running sum) / Z, C_{n_t-1} := 1, and the
+        // count of thresholds below each C_t (once per tile; the counts are
+        // made monotone across lanes below)
         double lrun = 0.0;
         int lcnt = 0;
         for (int t = tb; t < te; ++t) {
             lrun += (double)tstat[t].y * tf[t];
-            const double C = (t == nt - 1) ? 1.0 : (excl + lrun) / Z;
+            const double C = (t == nt - 1) ? 1.0 : (excl + lrun) * invZ;
             tC[t] = C;
-            lcnt = max(lcnt, thresholds_below(C, U, S));
+            const int c = thresholds_below(C, U, S);
+            tcn[t] = c;
+            lcnt = max(lcnt, c);
         }
         const int cmax = wave_incl_max_scan(lcnt, lane);
         int cpred = __shfl_up(cmax, 1);
@@ -243,7 +356,7 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
         {
             int cp = cpred;
             for (int t = tb; t < te; ++t) {
-                const int cnt = max(cp, thresholds_below(tC[t], U, S));
+                const int cnt = max(cp, tcn[t]);
                 nvl += cnt > cp;
                 cp = cnt;
             }
@@ -255,7 +368,7 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
             int cp = cpred;
             double cprev = Cpred;
             for (int t = tb; t < te; ++t) {
-                const int cnt = max(cp, thresholds_below(tC[t], U, S));
+                const int cnt = max(cp, tcn[t]);
                 const int St = cnt - cp;
                 if (tile_budget) tile_budget[(size_t)bh * max_nt + t] = St;
                 if (St > 0 && vpos < kcap) {
@@ -263,7 +376,7 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
                     rec.t = t;
                     rec.first = cp;
                     rec.cnt = St;
-                    rec.a = (float)((double)S * (tf[t] / Z));
+                    rec.a = (float)((double)S * tf[t] * invZ);
                     rec.b = (float)((double)S * (cprev - U));
                     vis[vpos] = rec;
                     ++vpos;

@@ -51,6 +51,16 @@ def test_prop_tiles_ragged_tail(gpu, T):
     _say("T", T, rep)
 
 
+@pytest.mark.parametrize("T,n", [(64, 4000), (64, 12000), (64, 20000), (128, 40000), (64, 65536)])
+def test_prop_many_tiles(gpu, T, n):
+    """Reducer paths by tiles per lane: n_t = 63, 188, 313, 313 and 1024 (the
+    maximum), i.e. 1, 3, 5, 5 and 16 tiles per reducer lane."""
+    import parity
+    cfg = synth.small_config(2, batch=1, seq_len=n, num_q_heads=8, num_kv_heads=2)
+    rep = parity.check_prop(_dev(cfg, 6, gpu, tile_len=T), 256)
+    _say("T", T, "n", n, rep)
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (32, 8), (16, 2)])
 def test_prop_gqa_groups(gpu, hq, hkv):
     import parity
