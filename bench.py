@@ -7,8 +7,11 @@ heads, 8 KV heads, head dim 128, bf16 KV, S = 128, tiles of 256 tokens
 (synthetic inputs with planted high-scoring keys and 4 sinks per KV head).
 Inputs are resident in HBM before timing starts; steps rotate over enough
 copies of the KV cache (>= 1 GiB) that the 256 MB Infinity Cache cannot hold
-them.  The same GPU's exact split-KV decode is timed the same way, and the
-fp64 CPU oracle is timed on a bounded sample on the host.
+them.  `value` comes from plain host calls, one per step (--mode eager, the
+default); replay of a captured HIP graph is reported beside it.  The same
+GPU's exact split-KV decode (and S2ANTA-flash, where the workload has a flash
+budget) is timed the same way, and the fp64 CPU oracle is timed on a bounded
+sample on the host.
 
 Prints one JSON line (see the "value"/"roofline"/"cpu_baseline" fields).
 """
@@ -59,14 +62,21 @@ def log(*a):
 
 
 def time_steps(fn, steps, warmup, events=None):
-    """Run fn(i) warmup times untimed then `steps` times timed; returns
-    (ms_per_step, per-step dominant-kernel ms list or None)."""
+    """Run fn(i) warmup times untimed, then `steps` times timed with plain
+    host calls; with `events`, run the steps once more with the dominant
+    kernel bracketed by dispatch-recorded events.  Returns (ms_per_step,
+    per-step dominant-kernel ms list or None)."""
     import torch
     import stochastic_sparse_attention_amd as sa
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    pairs = None
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = None
     if events:
         pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for _ in range(steps)]
@@ -74,19 +84,30 @@ def time_steps(fn, steps, warmup, events=None):
             a.record()
             b.record()
         torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        if pairs:
+        for i in range(steps):
             sa.santa_set_timing_events(pairs[i][0], pairs[i][1])
-        fn(warmup + i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    sa.santa_set_timing_events(None, None)
-    kern = None
-    if pairs:
+            fn(warmup + i)
+        torch.cuda.synchronize()
+        sa.santa_set_timing_events(None, None)
         kern = [a.elapsed_time(b) for a, b in pairs]
     return (t1 - t0) * 1e3 / steps, kern
+
+
+def step_spread(fn, steps, warmup):
+    """p10/p50/p90 of single-step GPU times: events recorded on the stream
+    between consecutive host calls."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        fn(warmup + i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    return {q: round(float(np.percentile(per, q)) * 1e3, 3) for q in (10, 50, 90)}
 
 
 def time_graph(step_fn, ncopy, steps, warmup):
@@ -204,9 +225,9 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 device copies of 256 MiB (known traffic: 256 MiB read and "
                          "256 MiB written each) to calibrate the FETCH_SIZE / WRITE_SIZE counters")
-    ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
-                    help="graph: steps replayed from a captured HIP graph (value); "
-                         "eager: one host call per step")
+    ap.add_argument("--mode", choices=["graph", "eager"], default="eager",
+                    help="which timing gives `value`: eager = one host call per step, "
+                         "graph = steps replayed from a captured HIP graph (both are reported)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -252,11 +273,11 @@ def main(argv=None):
 
     ms_eager, kern = time_steps(prop_step, args.steps, args.warmup, events=True)
     log(f"bench: prop eager {ms_eager * 1e3:.2f} us/step, pass-1 {np.mean(kern) * 1e3:.2f} us")
-    ms = ms_eager
-    spread = None
-    if args.mode == "graph":
-        ms, spread = time_graph(prop_step, ncopy, args.steps, args.warmup)
-        log(f"bench: prop graph {ms * 1e3:.2f} us/step (p10/p50/p90 {spread})")
+    eager_spread = step_spread(prop_step, args.steps, args.warmup)
+    ms_graph, spread = time_graph(prop_step, ncopy, args.steps, args.warmup)
+    log(f"bench: prop graph {ms_graph * 1e3:.2f} us/step (p10/p50/p90 {spread}); "
+        f"eager p10/p50/p90 {eager_spread}")
+    ms = ms_eager if args.mode == "eager" else ms_graph
 
     # one more call with the optional outputs, for the byte count and V-row share
     max_nt = (cfg.seq_len + T - 1) // T
@@ -296,8 +317,11 @@ def main(argv=None):
         "us_per_step": round(ms * 1e3, 3),
         "timing_mode": args.mode,
         "eager_us_per_step": round(ms_eager * 1e3, 3),
+        "graph_us_per_step": round(ms_graph * 1e3, 3),
         "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
-        "step_us_p10_p50_p90": spread,
+        "step_us_p10_p50_p90": spread if args.mode == "graph" else eager_spread,
+        "step_spread_note": "eager spread: events recorded between host calls (they add their own overhead); graph spread: per replay of the captured steps",
+        "graph_step_us_p10_p50_p90": spread,
         "copy_peak_GB/s": round(copy_gbs, 1),
         "pct_of_copy_peak": round(100 * step_gbs / copy_gbs, 2),
         "algorithmic_bytes_per_step": nbytes,
@@ -321,15 +345,15 @@ def main(argv=None):
             sa.exact_decode_ref(dev.problem, dev.q, ks[c], vs[c], oute, workspace=wse)
 
         ems_eager, ekern = time_steps(exact_step, args.steps, args.warmup, events=True)
-        ems = ems_eager
-        if args.mode == "graph":
-            ems, _espread = time_graph(exact_step, ncopy, args.steps, args.warmup)
+        ems_graph, _espread = time_graph(exact_step, ncopy, args.steps, args.warmup)
+        ems = ems_eager if args.mode == "eager" else ems_graph
         eb = BM.exact_step_bytes(cfg, T, seq)
-        log(f"bench: exact {ems * 1e3:.2f} us/step (eager {ems_eager * 1e3:.2f}), "
+        log(f"bench: exact {ems * 1e3:.2f} us/step (eager {ems_eager * 1e3:.2f}, graph {ems_graph * 1e3:.2f}), "
             f"partial {np.mean(ekern) * 1e3:.2f} us")
         result["exact_decode_ref"] = {
             "us_per_step": round(ems * 1e3, 3),
             "eager_us_per_step": round(ems_eager * 1e3, 3),
+            "graph_us_per_step": round(ems_graph * 1e3, 3),
             "GB/s": round(eb["total"] / (ems * 1e-3) / 1e9, 1),
             "pct_of_hbm_peak": round(100 * eb["total"] / (ems * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
             "partial_kernel_us": round(float(np.mean(ekern)) * 1e3, 3),
@@ -348,16 +372,16 @@ def main(argv=None):
             sa.santa_decode_flash(dev.problem, dev.q, ks[c], vs[c], Sf, uf, outf, workspace=wsf)
 
         fms_eager, fkern = time_steps(flash_step, args.steps, args.warmup, events=True)
-        fms = fms_eager
-        if args.mode == "graph":
-            fms, _fspread = time_graph(flash_step, ncopy, args.steps, args.warmup)
+        fms_graph, _fspread = time_graph(flash_step, ncopy, args.steps, args.warmup)
+        fms = fms_eager if args.mode == "eager" else fms_graph
         fb = BM.flash_step_bytes(cfg, Sf, T)
-        log(f"bench: flash S={Sf} {fms * 1e3:.2f} us/step (eager {fms_eager * 1e3:.2f}), "
+        log(f"bench: flash S={Sf} {fms * 1e3:.2f} us/step (eager {fms_eager * 1e3:.2f}, graph {fms_graph * 1e3:.2f}), "
             f"tile kernel {np.mean(fkern) * 1e3:.2f} us")
         result["santa_flash"] = {
             "S": Sf,
             "us_per_step": round(fms * 1e3, 3),
             "eager_us_per_step": round(fms_eager * 1e3, 3),
+            "graph_us_per_step": round(fms_graph * 1e3, 3),
             "GB/s": round(fb["total"] / (fms * 1e-3) / 1e9, 1),
             "pct_of_hbm_peak": round(100 * fb["total"] / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
             "tile_kernel_us": round(float(np.mean(fkern)) * 1e3, 3),
