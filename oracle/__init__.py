@@ -65,6 +65,7 @@ def lib():
         L.oracle_strat_thresholds.argtypes = [dp, C.c_int, dp]
         L.oracle_iid_thresholds.argtypes = [dp, C.c_int, dp]
         L.oracle_santa_prop.argtypes = [P, vp, vp, vp, C.c_int, fp, dp, ip, dp, ip]
+        L.oracle_santa_prop_sampler.argtypes = [P, vp, vp, vp, C.c_int, C.c_int, fp, dp, ip, dp, ip]
         L.oracle_santa_flash.argtypes = [P, vp, vp, vp, C.c_int, fp, dp, ip, dp, dp]
         L.oracle_exact.argtypes = [P, vp, vp, vp, dp]
         L.oracle_replay.argtypes = [P, vp, C.c_int, ip, dp, C.c_int, dp]
@@ -227,6 +228,27 @@ def santa_prop(prob: Problem, q, k, v, S, u):
                                  _dptr(out), _iptr(idx), _dptr(dl), _iptr(tc))
     if rc:
         raise ValueError(f"oracle_santa_prop: {rc}")
+    return {"out": out, "idx": idx, "delta": dl, "tile_counts": tc}
+
+
+SAMPLERS = {"sys": 0, "strat": 1, "iid": 2}
+
+
+def santa_prop_sampler(prob: Problem, q, k, v, S, sampler, u):
+    """S2ANTA-prop with the "sys", "strat" or "iid" threshold generator.
+    u: [B*Hq] offsets in [0, 1/S) for sys, [B*Hq, S] uniforms in [0,1) else."""
+    BH, d = prob.batch * prob.num_q_heads, prob.head_dim
+    u = np.ascontiguousarray(u, np.float32)
+    out = np.empty((BH, d), np.float64)
+    idx = np.empty((BH, S), np.int32)
+    dl = np.empty((BH, S), np.float64)
+    mnt = prob.max_tiles()
+    tc = np.empty((BH, mnt), np.int32)
+    rc = lib().oracle_santa_prop_sampler(prob.ref, _vp(q), _vp(k), _vp(v), S, SAMPLERS[sampler],
+                                         u.ctypes.data_as(C.POINTER(C.c_float)),
+                                         _dptr(out), _iptr(idx), _dptr(dl), _iptr(tc))
+    if rc:
+        raise ValueError(f"oracle_santa_prop_sampler: {rc}")
     return {"out": out, "idx": idx, "delta": dl, "tile_counts": tc}
 
 

@@ -249,21 +249,27 @@ static int max_tiles(const oracle_problem *p)
 }
 
 /* ------------------------------------------------------------------ */
-/* S2ANTA-sys over the whole KV cache (O1-O8).  By R4 this is exactly   */
-/* what S2ANTA-prop computes: tiles change how the thresholds are       */
-/* located, not which tokens they select [key design 2].                */
-/*   u        [B*Hq]   offsets, each in [0, 1/S)                        */
+/* S2ANTA-prop with a choice of threshold generator (O1-O8, O12).       */
+/* By R4 prop equals untiled sampling at the same thresholds: tiles     */
+/* change how the thresholds are located, not which tokens they select  */
+/* [key design 2].  The generator is that of key design 1:              */
+/*   kind 0  S2ANTA-sys:   u [B*Hq], one offset per head in [0, 1/S);   */
+/*                         t_m = U + m/S                                */
+/*   kind 1  S2ANTA-strat: u [B*Hq*S], one uniform in [0,1) per stratum; */
+/*                         t_m = (m + u_m)/S                            */
+/*   kind 2  i.i.d.:       u [B*Hq*S], uniforms in [0,1); t = sorted u  */
+/* (thresholds formed in fp64 from the fp32 inputs).                    */
 /*   out      [B*Hq*d] estimate (1/S) sum V[J_m]                        */
 /*   idx      [B*Hq*S] selected token per threshold (NULL allowed)     */
 /*   delta    [B*Hq*S] boundary distance per threshold (NULL allowed)  */
 /*   tile_cnt [B*Hq*max_nt] thresholds per tile, S_t (NULL allowed)    */
 /* Returns 0, or a negative code on bad arguments.                      */
 /* ------------------------------------------------------------------ */
-int oracle_santa_prop(const oracle_problem *p, const void *q, const void *k,
-                      const void *v, int S, const float *u, double *out,
-                      int *idx, double *delta, int *tile_cnt)
+int oracle_santa_prop_sampler(const oracle_problem *p, const void *q, const void *k,
+                              const void *v, int S, int kind, const float *u, double *out,
+                              int *idx, double *delta, int *tile_cnt)
 {
-    if (S <= 0 || !lengths_ok(p)) return -1;
+    if (S <= 0 || kind < 0 || kind > 2 || !lengths_ok(p)) return -1;
     int H = p->num_q_heads, d = p->head_dim, mnt = max_tiles(p);
     int status = 0;
     int nheads = p->batch * H;
@@ -283,16 +289,32 @@ int oracle_santa_prop(const oracle_problem *p, const void *q, const void *k,
         double *x = (double *)malloc(sizeof(double) * (size_t)n);
         double *e = (double *)malloc(sizeof(double) * (size_t)n);
         double *t = (double *)malloc(sizeof(double) * (size_t)S);
+        double *u01 = (double *)malloc(sizeof(double) * (size_t)S);
         int *J = (int *)malloc(sizeof(int) * (size_t)S);
         double *dl = (double *)malloc(sizeof(double) * (size_t)S);
         oracle_logits(p, q, k, b, h, x);
         oracle_softmax_weights(x, n, e, NULL);
-        double U = (double)u[bh];
-        if (!(U >= 0.0 && U < 1.0 / (double)S)) {
+        if (kind == 0) {
+            double U = (double)u[bh];
+            if (!(U >= 0.0 && U < 1.0 / (double)S)) {
 #pragma omp atomic write
-            status = -3;
+                status = -3;
+            }
+            oracle_sys_thresholds(U, S, t);
+        } else {
+            for (int m = 0; m < S; ++m) {
+                u01[m] = (double)u[(size_t)bh * S + m];
+                if (!(u01[m] >= 0.0 && u01[m] < 1.0)) {
+#pragma omp atomic write
+                    status = -3;
+                    u01[m] = 0.0;
+                }
+            }
+            if (kind == 1)
+                oracle_strat_thresholds(u01, S, t);
+            else
+                oracle_iid_thresholds(u01, S, t);
         }
-        oracle_sys_thresholds(U, S, t);
         if (oracle_invert_cdf(e, n, t, S, J, dl) != 0) {
 #pragma omp atomic write
             status = -4;
@@ -305,9 +327,17 @@ int oracle_santa_prop(const oracle_problem *p, const void *q, const void *k,
             for (int i = 0; i < mnt; ++i) tc[i] = 0;
             for (int m = 0; m < S; ++m) tc[J[m] / p->tile_len] += 1;
         }
-        free(x); free(e); free(t); free(J); free(dl);
+        free(x); free(e); free(t); free(u01); free(J); free(dl);
     }
     return status;
+}
+
+/* S2ANTA-sys prop: the systematic generator of the function above. */
+int oracle_santa_prop(const oracle_problem *p, const void *q, const void *k,
+                      const void *v, int S, const float *u, double *out,
+                      int *idx, double *delta, int *tile_cnt)
+{
+    return oracle_santa_prop_sampler(p, q, k, v, S, 0, u, out, idx, delta, tile_cnt);
 }
 
 /* ------------------------------------------------------------------ */

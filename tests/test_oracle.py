@@ -250,6 +250,97 @@ def test_prop_one_hot_end_to_end_is_exact_row():
         assert np.array_equal(r["out"][h], vv[0, g, 37 + 50 * g].astype(np.float64))
 
 
+@pytest.mark.parametrize("sampler", ["strat", "iid"])
+def test_prop_sampler_one_hot_is_exact_row(sampler):
+    """key design 1: whatever the thresholds, a one-hot A selects its token."""
+    inp, prob = _small_inputs(2, seq_len=512, batch=1, hot=0, sinks=0, tile_len=64)
+    G = inp.cfg.group
+    kv = inp.values("k").copy()
+    qv = inp.values("q")
+    for g in range(inp.cfg.num_kv_heads):
+        qbar = qv[0, g * G:(g + 1) * G]
+        kv[0, g] *= 0.0
+        kv[0, g, 11 + 60 * g] = np.sign(qbar.mean(0)) * 1024.0
+    inp.k = synth.f32_to_bf16_bits(kv)
+    S = 48
+    u = np.random.default_rng(7).random((inp.cfg.num_q_heads, S)).astype(np.float32)
+    r = O.santa_prop_sampler(prob, inp.q, inp.k, inp.v, S, sampler, u)
+    vv = inp.values("v")
+    for h in range(inp.cfg.num_q_heads):
+        g = h // G
+        assert np.all(r["idx"][h] == 11 + 60 * g)
+        assert np.array_equal(r["out"][h], vv[0, g, 11 + 60 * g].astype(np.float64))
+
+
+def _uniform_attention_inputs(n=1024):
+    """Identical keys: every logit is equal, A is exactly uniform and
+    F_j = (j + 1)/n holds exactly in fp64 for n a power of two."""
+    inp, prob = _small_inputs(2, seq_len=n, batch=1, hot=0, sinks=0, tile_len=128,
+                              num_q_heads=4, num_kv_heads=1)
+    kv = inp.values("k").copy()
+    kv[0, 0, :] = kv[0, 0, 0]
+    inp.k = synth.f32_to_bf16_bits(kv)
+    return inp, prob
+
+
+def test_prop_strat_with_S_equal_nk_on_uniform_A_is_mean():
+    """S2ANTA-strat with one stratum per token on uniform A: threshold m lies in
+    [m/n, (m+1)/n), so token m is chosen exactly once and the estimate is
+    the mean of V."""
+    n = 1024
+    inp, prob = _uniform_attention_inputs(n)
+    u = np.random.default_rng(3).random((4, n)).astype(np.float32)
+    r = O.santa_prop_sampler(prob, inp.q, inp.k, inp.v, n, "strat", u)
+    V = inp.values("v")[0, 0].astype(np.float64)
+    for h in range(4):
+        assert np.array_equal(r["idx"][h], np.arange(n))
+        np.testing.assert_allclose(r["out"][h], V.mean(0), rtol=0, atol=1e-12)
+
+
+def test_prop_iid_equal_uniforms_pick_one_token():
+    """i.i.d. with every uniform equal to c: all thresholds are c and, on
+    uniform A, all select token floor(c n)."""
+    n = 1024
+    inp, prob = _uniform_attention_inputs(n)
+    S = 40
+    u = np.full((4, S), 0.3, np.float32)
+    r = O.santa_prop_sampler(prob, inp.q, inp.k, inp.v, S, "iid", u)
+    j = int(np.floor(np.float64(np.float32(0.3)) * n))
+    V = inp.values("v")[0, 0].astype(np.float64)
+    assert np.all(r["idx"] == j)
+    for h in range(4):
+        assert np.array_equal(r["out"][h], V[j])
+
+
+@pytest.mark.parametrize("sampler", ["strat", "iid"])
+def test_prop_sampler_invariants(sampler):
+    """Indices are nondecreasing in m (sorted thresholds), budgets sum to S,
+    and for strat every tile's budget differs from S * p_t by less than 2
+    (each stratum holds one threshold; only the two strata cut by the tile's
+    CDF edges can go either way)."""
+    inp, prob = _small_inputs(2, seq_len=2048, batch=2, tile_len=256)
+    S, T = 96, 256
+    H = inp.cfg.num_q_heads
+    u = np.random.default_rng(11).random((2 * H, S)).astype(np.float32)
+    r = O.santa_prop_sampler(prob, inp.q, inp.k, inp.v, S, sampler, u)
+    assert np.all(np.diff(r["idx"], axis=1) >= 0)
+    assert np.all(r["tile_counts"].sum(1) == S)
+    if sampler == "strat":
+        for bh in range(2 * H):
+            b, h = divmod(bh, H)
+            e, z, _ = O.softmax_weights(O.logits(prob, inp.q, inp.k, b, h))
+            p = np.array([e[t * T:(t + 1) * T].sum() for t in range(e.size // T)]) / z
+            assert np.all(np.abs(r["tile_counts"][bh] - S * p) < 2)
+
+
+def test_prop_sampler_rejects_out_of_range_uniforms():
+    inp, prob = _small_inputs(1)
+    u = np.zeros((1, 16), np.float32)
+    u[0, 3] = 1.0
+    with pytest.raises(ValueError):
+        O.santa_prop_sampler(prob, inp.q, inp.k, inp.v, 16, "strat", u)
+
+
 def test_prop_expectation_equals_exact():
     """E_U[S2ANTA-sys] = AV, by exact enumeration on the oracle's own weights."""
     for seed in (1, 2):
