@@ -120,6 +120,35 @@ int santa_decode_prop(const santa_problem *p, const void *q, const void *k, cons
                       int32_t *tile_budget, void *workspace, size_t workspace_bytes,
                       void *stream);
 
+/* Threshold generators of prop ("key design 1"). */
+typedef enum {
+    SANTA_SAMPLER_SYS = 0,     /* S2ANTA-sys: t_m = U + m/S, one offset U per head   */
+    SANTA_SAMPLER_STRAT = 1,   /* S2ANTA-strat: t_m = (m + u_m)/S, one uniform per
+                                  stratum [m/S, (m+1)/S)                            */
+    SANTA_SAMPLER_IID = 2      /* plain SANTA: t = the S uniforms, sorted (i.i.d.
+                                  draws from A, as in the Eq. (4) estimator)         */
+} santa_sampler;
+
+/*
+ * S2ANTA-prop with a choice of threshold generator ("key design 1"; the
+ * schedule is that of santa_decode_prop, which is this call with
+ * SANTA_SAMPLER_SYS).  Tile budgets are the numbers of thresholds in each
+ * tile's CDF interval for every generator, so sum_t S_t = S.
+ *
+ *   sampler      a santa_sampler value (else SANTA_ERR_INVALID)
+ *   u            SANTA_SAMPLER_SYS: [B*Hq] offsets in [0, 1/S);
+ *                STRAT and IID: [B*Hq, S] uniforms in [0, 1).  The device
+ *                does not check them: values outside the range are clamped
+ *                into it (NaN counts as 0).  STRAT and IID thresholds are
+ *                formed in fp64 (IID sorted on the device).
+ *   other arguments and the workspace as for santa_decode_prop; the
+ *   threshold list lives in LDS (S doubles, a power of two for IID).
+ */
+int santa_decode_prop_sampler(const santa_problem *p, const void *q, const void *k, const void *v,
+                              int32_t S, int32_t sampler, const float *u, float *out,
+                              int32_t *sample_idx, int32_t *tile_budget, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 /*
  * S2ANTA-flash ("key design 3").  No global step between scoring and
  * sampling: each tile of T tokens takes S_f = S / n_t samples from its own

@@ -12,10 +12,10 @@ from __future__ import annotations
 import ctypes as C
 
 from . import _lib
-from ._lib import SantaError, santa_problem, SANTA_F32, SANTA_BF16, VARIANT
+from ._lib import SantaError, santa_problem, SANTA_F32, SANTA_BF16, VARIANT, SAMPLER
 
 __all__ = [
-    "Problem", "santa_workspace_size", "santa_decode_prop", "santa_decode_flash",
+    "Problem", "santa_workspace_size", "santa_decode_prop", "santa_decode_prop_sampler", "santa_decode_flash",
     "exact_decode_ref", "santa_set_timing_events", "SantaError",
 ]
 
@@ -73,6 +73,17 @@ def santa_decode_prop(problem: Problem, q, k, v, S, u, out, sample_idx=None, til
                                        _ptr(sample_idx), _ptr(tile_budget), _ptr(ws), ws.numel(),
                                        _stream(stream))
     _lib._check("santa_decode_prop", st)
+    return ws
+
+
+def santa_decode_prop_sampler(problem: Problem, q, k, v, S, sampler, u, out, sample_idx=None,
+                              tile_budget=None, workspace=None, stream=None):
+    """sampler: "sys" (u: [B*Hq] offsets), "strat" or "iid" (u: [B*Hq, S] uniforms)."""
+    ws = _workspace(problem, "prop", S, workspace, q.device)
+    st = _lib.load().santa_decode_prop_sampler(problem.ref, _ptr(q), _ptr(k), _ptr(v), S, SAMPLER[sampler],
+                                               _ptr(u), _ptr(out), _ptr(sample_idx), _ptr(tile_budget),
+                                               _ptr(ws), ws.numel(), _stream(stream))
+    _lib._check("santa_decode_prop_sampler", st)
     return ws
 
 

@@ -18,9 +18,11 @@ LIB_PATH = os.environ.get("SANTA_LIB") or os.path.join(HERE, "libsanta.so")
 SANTA_OK, SANTA_ERR_INVALID, SANTA_ERR_UNSUPPORTED, SANTA_ERR_WORKSPACE, SANTA_ERR_HIP = 0, -1, -2, -3, -4
 SANTA_F32, SANTA_BF16 = 0, 1
 VARIANT = {"prop": 0, "flash": 1, "exact": 2}
+SAMPLER = {"sys": 0, "strat": 1, "iid": 2}
 
 EXPORTS = [
-    "santa_workspace_size", "santa_decode_prop", "santa_decode_flash", "exact_decode_ref",
+    "santa_workspace_size", "santa_decode_prop", "santa_decode_prop_sampler", "santa_decode_flash",
+    "exact_decode_ref",
     "santa_set_timing_events", "santa_status_string", "santa_abi_version",
 ]
 
@@ -62,6 +64,8 @@ def load():
     sampled = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     L.santa_decode_prop.argtypes = sampled
     L.santa_decode_prop.restype = C.c_int
+    L.santa_decode_prop_sampler.argtypes = [P, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.santa_decode_prop_sampler.restype = C.c_int
     L.santa_decode_flash.argtypes = sampled
     L.santa_decode_flash.restype = C.c_int
     L.exact_decode_ref.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]

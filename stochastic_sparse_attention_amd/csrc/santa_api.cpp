@@ -137,19 +137,22 @@ santa::LaunchArgs make_args(const santa_problem *p, const Derived &d, const void
 }
 
 int run_sampled(int variant, const santa_problem *p, const void *q, const void *k, const void *v,
-                int32_t S, const float *u, float *out, int32_t *sample_idx, int32_t *tile_budget,
-                void *workspace, size_t workspace_bytes, void *stream) {
+                int32_t S, int32_t sampler, const float *u, float *out, int32_t *sample_idx,
+                int32_t *tile_budget, void *workspace, size_t workspace_bytes, void *stream) {
     Derived d;
     int st = validate(p, variant, S, &d);
     if (st != SANTA_OK) return st;
+    if (sampler != SANTA_SAMPLER_SYS && sampler != SANTA_SAMPLER_STRAT && sampler != SANTA_SAMPLER_IID)
+        return SANTA_ERR_INVALID;
     if (p->batch == 0) return SANTA_OK;
     if (!q || !k || !v || !u || !out) return SANTA_ERR_INVALID;
     santa::Workspace ws;
     st = check_workspace(p, variant, d, workspace, workspace_bytes, &ws);
     if (st != SANTA_OK) return st;
-    const santa::LaunchArgs a =
+    santa::LaunchArgs a =
         make_args(p, d, q, k, v, S, u, out, sample_idx,
                   variant == SANTA_VARIANT_PROP ? tile_budget : nullptr, ws, stream);
+    a.sampler = sampler;
     const santa::TimingHook hook{g_ev_begin, g_ev_end};
     const hipError_t e = variant == SANTA_VARIANT_PROP ? santa::launch_prop(a, hook)
                                                        : santa::launch_flash(a, hook);
@@ -172,15 +175,23 @@ int santa_workspace_size(const santa_problem *p, int32_t variant, int32_t S, siz
 int santa_decode_prop(const santa_problem *p, const void *q, const void *k, const void *v, int32_t S,
                       const float *u, float *out, int32_t *sample_idx, int32_t *tile_budget,
                       void *workspace, size_t workspace_bytes, void *stream) {
-    return run_sampled(SANTA_VARIANT_PROP, p, q, k, v, S, u, out, sample_idx, tile_budget, workspace,
-                       workspace_bytes, stream);
+    return run_sampled(SANTA_VARIANT_PROP, p, q, k, v, S, SANTA_SAMPLER_SYS, u, out, sample_idx, tile_budget,
+                       workspace, workspace_bytes, stream);
+}
+
+int santa_decode_prop_sampler(const santa_problem *p, const void *q, const void *k, const void *v,
+                              int32_t S, int32_t sampler, const float *u, float *out,
+                              int32_t *sample_idx, int32_t *tile_budget, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    return run_sampled(SANTA_VARIANT_PROP, p, q, k, v, S, sampler, u, out, sample_idx, tile_budget,
+                       workspace, workspace_bytes, stream);
 }
 
 int santa_decode_flash(const santa_problem *p, const void *q, const void *k, const void *v, int32_t S,
                        const float *u, float *out, int32_t *sample_idx, int32_t *tile_budget,
                        void *workspace, size_t workspace_bytes, void *stream) {
-    return run_sampled(SANTA_VARIANT_FLASH, p, q, k, v, S, u, out, sample_idx, tile_budget, workspace,
-                       workspace_bytes, stream);
+    return run_sampled(SANTA_VARIANT_FLASH, p, q, k, v, S, SANTA_SAMPLER_SYS, u, out, sample_idx, tile_budget,
+                       workspace, workspace_bytes, stream);
 }
 
 int exact_decode_ref(const santa_problem *p, const void *q, const void *k, const void *v, float *out,
@@ -220,6 +231,6 @@ const char *santa_status_string(int status) {
     }
 }
 
-int santa_abi_version(void) { return 1; }
+int santa_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -1,5 +1,6 @@
 // santa_launch.h -- host-side interface between the C ABI (santa_api.cpp)
-// and the kernel launchers (santa_kernels.hip).  Internal to libsanta.
+// and the kernel launchers (santa_prop.hip, santa_flash.hip, santa_exact.hip).
+// Internal to libsanta.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,6 +8,18 @@
 #include <stdint.h>
 
 namespace santa {
+
+// threshold generators of prop (the values of santa_sampler)
+constexpr int kSamplerSys = 0, kSamplerStrat = 1, kSamplerIid = 2;
+
+// LDS slots of a head's threshold list: S, or the next power of two for
+// the i.i.d. generator, whose uniforms are sorted with a bitonic network
+__host__ __device__ inline int threshold_slots(int S, int sampler) {
+    if (sampler != kSamplerIid) return S;
+    int p = 1;
+    while (p < S) p <<= 1;
+    return p;
+}
 
 // Carved workspace regions (device pointers; unused ones are null).
 struct Workspace {
@@ -33,6 +46,7 @@ struct LaunchArgs {
     int *sample_idx;
     int *tile_budget;
     int kmax;   // prop: visit-list capacity per head
+    int sampler;   // prop: kSamplerSys / kSamplerStrat / kSamplerIid
     Workspace ws;
     void *stream;
 };
@@ -46,5 +60,6 @@ hipError_t launch_prop(const LaunchArgs &a, const TimingHook &hook);
 hipError_t launch_flash(const LaunchArgs &a, const TimingHook &hook);
 hipError_t launch_exact(const LaunchArgs &a, const TimingHook &hook);
 size_t visit_record_bytes();
+size_t prop_sample_lds_bytes(int kcap, int S, int sampler);
 
 }  // namespace santa

@@ -120,11 +120,13 @@ __global__ __launch_bounds__(kBlock) void prop_pass1_kernel(
 // (16 lanes per row, 4 rows per wave instruction) and accumulates
 // multiplicity * row; the waves' sums are added in a fixed order and
 // divided by S.
-// Visit record of a tile with S_t > 0: its thresholds are first .. first+cnt-1
-// and the number of thresholds below the CDF position of its element j is
-// ceil(P_j * a + b), with P_j the stash prefix, a = S e^{scale(m_t-M)}/Z and
-// b = S (C_{t-1} - U) (formed in fp64, rounded to fp32: the rounding moves a
-// threshold by ~1e-7 in CDF units).
+// Visit record of a tile with S_t > 0: its thresholds are first .. first+cnt-1.
+// Systematic thresholds: the number of thresholds below the CDF position of
+// its element j is ceil(P_j * a + b), with P_j the stash prefix,
+// a = S e^{scale(m_t-M)}/Z and b = S (C_{t-1} - U).  Stratified and i.i.d.
+// thresholds: P_j * a + b is that CDF position itself (a = e^{scale(m_t-M)}/Z,
+// b = C_{t-1}).  Both are formed in fp64 and rounded to fp32; the rounding
+// moves a threshold by ~1e-7 in CDF units.
 struct VisitRec {
     int t, first, cnt;
     float a, b;
@@ -150,13 +152,45 @@ __device__ __forceinline__ void load_stash(const float *p, float (&e)[EPL]) {
     }
 }
 
+// Threshold counts: the number of thresholds strictly below a CDF position.
+// Systematic thresholds U + m/S have the closed form; the stratified and
+// i.i.d. generators give a sorted list in LDS, searched by bisection.
+struct SysCount {
+    double U;
+    int S;
+    __device__ __forceinline__ int operator()(double C) const { return thresholds_below(C, U, S); }
+    // visit record: count below the position of token j = ceil(P_j a + b)
+    __device__ __forceinline__ void rec_ab(double f, double invZ, double cprev, float &a, float &b) const {
+        a = (float)((double)S * f * invZ);
+        b = (float)((double)S * (cprev - U));
+    }
+};
+struct ListCount {
+    const double *thr;    // [S], nondecreasing, in [0, 1)
+    int S;
+    __device__ __forceinline__ int operator()(double C) const {
+        int lo = 0, hi = S;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (thr[mid] < C) lo = mid + 1;
+            else hi = mid;
+        }
+        return lo;
+    }
+    // visit record: CDF position of token j = P_j a + b
+    __device__ __forceinline__ void rec_ab(double f, double invZ, double cprev, float &a, float &b) const {
+        a = (float)(f * invZ);
+        b = (float)cprev;
+    }
+};
+
 // Reducer of one head on one wave, with each lane's tiles (at most CHR of
 // them: lane l owns tiles [l*CH, l*CH + CH), CH = ceil(n_t/64)) held in
 // registers.  Writes the visit list, its length and the optional budgets.
-// The arithmetic and its order are those of the LDS variant in the kernel.
-template <int CHR>
-__device__ __forceinline__ void reduce_in_registers(const float2 *__restrict__ stp, int nt, int lane, double U,
-                                                    int S, float scale, int kcap, VisitRec *vis,
+// The arithmetic and its order are those of the LDS variant below.
+template <int CHR, class CNT>
+__device__ __forceinline__ void reduce_in_registers(const float2 *__restrict__ stp, int nt, int lane, const CNT &count,
+                                                    float scale, int kcap, VisitRec *vis,
                                                     int *__restrict__ budget, int max_nt, int &nvis_out) {
     const int CH = (nt + 63) / 64;
     const int tb = lane * CH;
@@ -169,7 +203,9 @@ __device__ __forceinline__ void reduce_in_registers(const float2 *__restrict__ s
         lmaxv = fmaxf(lmaxv, st[i].x);
     }
     const float Mf = wave_max(lmaxv);
-    // tile weight e^{scale (m_t - M)} in fp32 (see the LDS variant)
+    // tile weight e^{scale (m_t - M)} in fp32: its rounding moves a tile's
+    // CDF interval by ~1e-7 of the tile's own mass, and the same value is
+    // used for C_t and for the pass-2 mapping, so the two stay consistent
     const float c2 = scale * 1.4426950408889634f;
     double f[CHR];
     double lsum = 0.0;
@@ -193,7 +229,7 @@ __device__ __forceinline__ void reduce_in_registers(const float2 *__restrict__ s
         const bool ok = i < CH && tb + i < nt;
         if (ok) lrun += (double)st[i].y * f[i];
         C[i] = (tb + i == nt - 1) ? 1.0 : (excl + lrun) * invZ;
-        c[i] = thresholds_below(C[i], U, S);
+        c[i] = ok ? count(C[i]) : 0;
         if (ok) {
             lcnt = max(lcnt, c[i]);
             clast = C[i];
@@ -235,8 +271,7 @@ __device__ __forceinline__ void reduce_in_registers(const float2 *__restrict__ s
                 rec.t = t;
                 rec.first = cp;
                 rec.cnt = St;
-                rec.a = (float)((double)S * f[i] * invZ);
-                rec.b = (float)((double)S * (cprev - U));
+                count.rec_ab(f[i], invZ, cprev, rec.a, rec.b);
                 vis[vpos] = rec;
                 ++vpos;
             }
@@ -248,18 +283,138 @@ __device__ __forceinline__ void reduce_in_registers(const float2 *__restrict__ s
         for (int t = nt + lane; t < max_nt; t += 64) budget[t] = 0;
 }
 
+// Per-tile arrays of the LDS reducer (more than 4 tiles per lane).
+struct ReducerLds {
+    float2 *tstat;    // (m_t, Z_t)
+    double *tf;       // e^{scale (m_t - M)}
+    double *tC;       // tile CDF C_t
+    int *tcn;         // thresholds below C_t
+};
+
+template <class CNT>
+__device__ __forceinline__ void reduce_with_lds(const float2 *__restrict__ stp, int nt, int lane, const CNT &count,
+                                                float scale, int kcap, VisitRec *vis, int *__restrict__ budget,
+                                                int max_nt, int &nvis_out, const ReducerLds &R) {
+    const int CH = (nt + 63) / 64;
+    const int tb = lane * CH, te = min(nt, tb + CH);
+    float lmaxv = -INFINITY;
+    for (int t = tb; t < te; ++t) {
+        const float2 v2 = stp[t];
+        R.tstat[t] = v2;
+        lmaxv = fmaxf(lmaxv, v2.x);
+    }
+    const float Mf = wave_max(lmaxv);
+    const float c2 = scale * 1.4426950408889634f;
+    double lsum = 0.0;
+    for (int t = tb; t < te; ++t) {
+        const float2 v2 = R.tstat[t];
+        const double f = (double)exp2f((v2.x - Mf) * c2);
+        R.tf[t] = f;
+        lsum += (double)v2.y * f;
+    }
+    const double incl = wave_incl_scan(lsum, lane);
+    double excl = __shfl_up(incl, 1);
+    if (lane == 0) excl = 0.0;
+    const double Z = __shfl(incl, 63);
+    const double invZ = 1.0 / Z;
+    // C_t = (excl + lane-local running sum) / Z, C_{n_t-1} := 1, and the
+    // count of thresholds below each C_t (once per tile; the counts are
+    // made monotone across lanes below)
+    double lrun = 0.0;
+    int lcnt = 0;
+    for (int t = tb; t < te; ++t) {
+        lrun += (double)R.tstat[t].y * R.tf[t];
+        const double C = (t == nt - 1) ? 1.0 : (excl + lrun) * invZ;
+        R.tC[t] = C;
+        const int c = count(C);
+        R.tcn[t] = c;
+        lcnt = max(lcnt, c);
+    }
+    const int cmax = wave_incl_max_scan(lcnt, lane);
+    int cpred = __shfl_up(cmax, 1);
+    double Cpred = __shfl_up(te > tb ? R.tC[te - 1] : 0.0, 1);      // C of the previous lane's last tile
+    if (lane == 0) {
+        cpred = 0;
+        Cpred = 0.0;
+    }
+    // visited tiles of this lane, then their positions in the visit list
+    int nvl = 0;
+    {
+        int cp = cpred;
+        for (int t = tb; t < te; ++t) {
+            const int cnt = max(cp, R.tcn[t]);
+            nvl += cnt > cp;
+            cp = cnt;
+        }
+    }
+    const int vincl = wave_incl_scan(nvl, lane);
+    int vpos = vincl - nvl;
+    if (lane == 63) nvis_out = vincl;
+    int cp = cpred;
+    double cprev = Cpred;
+    for (int t = tb; t < te; ++t) {
+        const int cnt = max(cp, R.tcn[t]);
+        const int St = cnt - cp;
+        if (budget) budget[t] = St;
+        if (St > 0 && vpos < kcap) {
+            VisitRec rec;
+            rec.t = t;
+            rec.first = cp;
+            rec.cnt = St;
+            count.rec_ab(R.tf[t], invZ, cprev, rec.a, rec.b);
+            vis[vpos] = rec;
+            ++vpos;
+        }
+        cp = cnt;
+        cprev = R.tC[t];
+    }
+    if (budget)
+        for (int t = nt + lane; t < max_nt; t += 64) budget[t] = 0;
+}
+
+template <class CNT>
+__device__ __forceinline__ void reduce_head(const float2 *__restrict__ stp, int nt, int lane, const CNT &count,
+                                            float scale, int kcap, VisitRec *vis, int *__restrict__ budget,
+                                            int max_nt, int &nvis_out, const ReducerLds &R) {
+    if (nt <= 64)
+        reduce_in_registers<1>(stp, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out);
+    else if (nt <= 128)
+        reduce_in_registers<2>(stp, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out);
+    else if (nt <= 256)
+        reduce_in_registers<4>(stp, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out);
+    else
+        reduce_with_lds(stp, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out, R);
+}
+
+// #{m in [0, len) : thr[m] < F} for a nondecreasing list
+__device__ __forceinline__ int count_below(const double *thr, int len, double F) {
+    int lo = 0, hi = len;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (thr[mid] < F) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
 // at most 64 VGPRs (8 waves per SIMD), so that two of these 1024-thread
 // workgroups share a compute unit
-template <typename KV, int T, bool PAGED>
+// LIST: stratified / i.i.d. thresholds (a sorted list in LDS); else the
+// systematic closed form
+template <typename KV, int T, bool PAGED, bool LIST>
 __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8))) void prop_sample_kernel(
     const KV *__restrict__ v, KVLayout L, const int *__restrict__ seq_lens, int batch, int num_q_heads,
-    int G, int S, int max_nt, int kcap, const float *__restrict__ u, float scale,
+    int G, int S, int max_nt, int kcap, int sampler, const float *__restrict__ u, float scale,
     const float *__restrict__ stash, const float2 *__restrict__ stats, float *__restrict__ out,
     int *__restrict__ sample_idx, int *__restrict__ tile_budget) {
-    constexpr int EPL = T / 64;
     extern __shared__ __align__(16) unsigned char smem[];
-    VisitRec *vis = reinterpret_cast<VisitRec *>(smem);                  // [kcap]
-    int *jsel = reinterpret_cast<int *>(smem + (size_t)kcap * sizeof(VisitRec));   // [S] marker rows, -1 elsewhere
+    // stratified / i.i.d.: the sorted thresholds first (padded to a power of
+    // two for the sort), then the visit list and the marker arrays
+    constexpr bool list = LIST;
+    const int np = list ? threshold_slots(S, sampler) : 0;
+    double *thr = reinterpret_cast<double *>(smem);                                     // [np]
+    VisitRec *vis = reinterpret_cast<VisitRec *>(smem + (size_t)np * sizeof(double));   // [kcap]
+    int *jsel = reinterpret_cast<int *>(smem + (size_t)np * sizeof(double) + (size_t)kcap * sizeof(VisitRec));   // [S] marker rows, -1 elsewhere
     int *jmul = jsel + S;                                                  // [S] marker multiplicities
     __shared__ float red[kSampleWaves][kHeadDim];
     __shared__ float2 tstat[kMaxTilesLds];          // reducer: per-tile (m_t, Z_t)
@@ -288,105 +443,56 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
         if (tid < kHeadDim) out[(size_t)bh * kHeadDim + tid] = 0.f;
         return;
     }
-    const double U = (double)u[bh];
+    // ---------------- thresholds of the stratified and i.i.d. generators:
+    // (m + u_m)/S, or the uniforms sorted, in fp64 (inputs outside [0,1)
+    // are clamped into it; NaN counts as 0)
+    if constexpr (LIST) {
+        const float *ub = u + (size_t)bh * S;
+        const double kBelowOne = 1.0 - 0x1p-53;
+        for (int m = tid; m < np; m += kSampleBlock) {
+            double x = INFINITY;                        // sort padding
+            if (m < S) {
+                x = (double)ub[m];
+                x = x >= 0.0 ? x : 0.0;
+                if (sampler == kSamplerStrat) x = ((double)m + x) / (double)S;
+                x = x < kBelowOne ? x : kBelowOne;
+            }
+            thr[m] = x;
+        }
+        __syncthreads();
+        if (sampler == kSamplerIid) {
+            // bitonic sort of the np slots, ascending
+            for (int k2 = 2; k2 <= np; k2 <<= 1) {
+                for (int j2 = k2 >> 1; j2 > 0; j2 >>= 1) {
+                    for (int i = tid; i < np; i += kSampleBlock) {
+                        const int p = i ^ j2;
+                        if (p > i) {
+                            const double a = thr[i], c = thr[p];
+                            const bool up = (i & k2) == 0;
+                            if ((a > c) == up) {
+                                thr[i] = c;
+                                thr[p] = a;
+                            }
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
+        }
+    }
 
     // ---------------- reducer: wave 0, lane l owns tiles [l*CH, l*CH + CH);
     // the other waves clear the marker positions meanwhile
     if (w != 0) {
         for (int m = tid - kWave; m < S; m += kSampleBlock - kWave) jsel[m] = -1;
-    } else if (nt <= 256) {
+    } else {
         const float2 *stp = stats + (size_t)bh * max_nt;
         int *budget = tile_budget ? tile_budget + (size_t)bh * max_nt : nullptr;
-        if (nt <= 64)
-            reduce_in_registers<1>(stp, nt, lane, U, S, scale, kcap, vis, budget, max_nt, nvis_sh);
-        else if (nt <= 128)
-            reduce_in_registers<2>(stp, nt, lane, U, S, scale, kcap, vis, budget, max_nt, nvis_sh);
+        const ReducerLds R{tstat, tf, tC, tcn};
+        if constexpr (!LIST)
+            reduce_head(stp, nt, lane, SysCount{(double)u[bh], S}, scale, kcap, vis, budget, max_nt, nvis_sh, R);
         else
-            reduce_in_registers<4>(stp, nt, lane, U, S, scale, kcap, vis, budget, max_nt, nvis_sh);
-    } else {
-        // more than 4 tiles per lane: per-tile values staged in LDS
-        const int CH = (nt + 63) / 64;
-        const int tb = lane * CH, te = min(nt, tb + CH);
-        const float2 *stp = stats + (size_t)bh * max_nt;
-        float lmaxv = -INFINITY;
-        for (int t = tb; t < te; ++t) {
-            const float2 v2 = stp[t];
-            tstat[t] = v2;
-            lmaxv = fmaxf(lmaxv, v2.x);
-        }
-        const float Mf = wave_max(lmaxv);
-        // tile weight e^{scale (m_t - M)} in fp32: its rounding moves a tile's
-        // CDF interval by ~1e-7 of the tile's own mass, and the same value is
-        // used for C_t and for the pass-2 mapping, so the two stay consistent
-        const float c2 = scale * 1.4426950408889634f;
-        double lsum = 0.0;
-        for (int t = tb; t < te; ++t) {
-            const float2 v2 = tstat[t];
-            const double f = (double)exp2f((v2.x - Mf) * c2);
-            tf[t] = f;
-            lsum += (double)v2.y * f;
-        }
-        const double incl = wave_incl_scan(lsum, lane);
-        double excl = __shfl_up(incl, 1);
-        if (lane == 0) excl = 0.0;
-        const double Z = __shfl(incl, 63);
-        const double invZ = 1.0 / Z;
-        // C_t = (excl + lane-local running sum) / Z, C_{n_t-1} := 1, and the
-        // count of thresholds below each C_t (once per tile; the counts are
-        // made monotone across lanes below)
-        double lrun = 0.0;
-        int lcnt = 0;
-        for (int t = tb; t < te; ++t) {
-            lrun += (double)tstat[t].y * tf[t];
-            const double C = (t == nt - 1) ? 1.0 : (excl + lrun) * invZ;
-            tC[t] = C;
-            const int c = thresholds_below(C, U, S);
-            tcn[t] = c;
-            lcnt = max(lcnt, c);
-        }
-        const int cmax = wave_incl_max_scan(lcnt, lane);
-        int cpred = __shfl_up(cmax, 1);
-        double Cpred = __shfl_up(te > tb ? tC[te - 1] : 0.0, 1);      // C of the previous lane's last tile
-        if (lane == 0) {
-            cpred = 0;
-            Cpred = 0.0;
-        }
-        // visited tiles of this lane, then their positions in the visit list
-        int nvl = 0;
-        {
-            int cp = cpred;
-            for (int t = tb; t < te; ++t) {
-                const int cnt = max(cp, tcn[t]);
-                nvl += cnt > cp;
-                cp = cnt;
-            }
-        }
-        const int vincl = wave_incl_scan(nvl, lane);
-        int vpos = vincl - nvl;
-        if (lane == 63) nvis_sh = vincl;
-        {
-            int cp = cpred;
-            double cprev = Cpred;
-            for (int t = tb; t < te; ++t) {
-                const int cnt = max(cp, tcn[t]);
-                const int St = cnt - cp;
-                if (tile_budget) tile_budget[(size_t)bh * max_nt + t] = St;
-                if (St > 0 && vpos < kcap) {
-                    VisitRec rec;
-                    rec.t = t;
-                    rec.first = cp;
-                    rec.cnt = St;
-                    rec.a = (float)((double)S * tf[t] * invZ);
-                    rec.b = (float)((double)S * (cprev - U));
-                    vis[vpos] = rec;
-                    ++vpos;
-                }
-                cp = cnt;
-                cprev = tC[t];
-            }
-        }
-        if (tile_budget)
-            for (int t = nt + lane; t < max_nt; t += 64) tile_budget[(size_t)bh * max_nt + t] = 0;
+            reduce_head(stp, nt, lane, ListCount{thr, S}, scale, kcap, vis, budget, max_nt, nvis_sh, R);
     }
     __syncthreads();
     const int nvis = min(nvis_sh, kcap);
@@ -424,24 +530,43 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
         const float bl = fmaf(excl, rec.a, rec.b);
         const int lo = rec.first, hi = rec.first + rec.cnt;
         const float fhi = (float)hi;
-        const int yl = max((int)fminf(ceilf(fmaf(e[EPL2 - 1], rec.a, bl)), fhi), lo);
+        // count reached at the lane's last token: systematic, the closed
+        // form; stratified / i.i.d., a bisection over the tile's thresholds
+        // at the CDF position P a + b
+        const int yl = list ? lo + count_below(thr + lo, hi - lo, (double)fmaf(e[EPL2 - 1], rec.a, bl))
+                            : max((int)fminf(ceilf(fmaf(e[EPL2 - 1], rec.a, bl)), fhi), lo);
         const int gmax = group_incl_max<LPT>(yl);
         int prev = __shfl_up(gmax, 1);                     // count reached by the earlier lanes
         if (gl == 0) prev = lo;
         if (active && yl > prev) {                         // thresholds prev .. yl-1 fall on this lane
             int yp = prev;
+            // a step can fall on a token of zero weight only through fp32
+            // rounding across lanes (a threshold within ~1e-7 of that
+            // token's CDF position); past the sequence end such a token is
+            // replaced by the last one, so every row read is inside the
+            // request
+            if constexpr (!LIST) {
 #pragma unroll
-            for (int qq = 0; qq < EPL2; ++qq) {
-                const int y = (int)fminf(ceilf(fmaf(e[qq], rec.a, bl)), fhi);
-                if (y > yp) {
-                    // a step can fall on a token of zero weight only through
-                    // fp32 rounding across lanes (a threshold within ~1e-7 of
-                    // that token's CDF position); past the sequence end such
-                    // a token is replaced by the last one, so every row read
-                    // is inside the request
-                    jsel[yp] = min(start + gl * EPL2 + qq, n - 1);
-                    jmul[yp] = y - yp;
-                    yp = y;
+                for (int qq = 0; qq < EPL2; ++qq) {
+                    const int y = (int)fminf(ceilf(fmaf(e[qq], rec.a, bl)), fhi);
+                    if (y > yp) {
+                        jsel[yp] = min(start + gl * EPL2 + qq, n - 1);
+                        jmul[yp] = y - yp;
+                        yp = y;
+                    }
+                }
+            } else {
+                // merge of the lane's tokens with its thresholds
+#pragma unroll
+                for (int qq = 0; qq < EPL2; ++qq) {
+                    const double Fq = (double)fmaf(e[qq], rec.a, bl);
+                    int y = yp;
+                    while (y < yl && thr[y] < Fq) ++y;
+                    if (y > yp) {
+                        jsel[yp] = min(start + gl * EPL2 + qq, n - 1);
+                        jmul[yp] = y - yp;
+                        yp = y;
+                    }
                 }
             }
         }
@@ -535,8 +660,9 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
 // ===================================================================
 // launchers
 // ===================================================================
-size_t prop_sample_lds_bytes(int kcap, int S) {
-    return (size_t)kcap * sizeof(VisitRec) + 2 * (size_t)S * sizeof(int);
+size_t prop_sample_lds_bytes(int kcap, int S, int sampler) {
+    const size_t thr = sampler == kSamplerSys ? 0 : (size_t)threshold_slots(S, sampler) * sizeof(double);
+    return thr + (size_t)kcap * sizeof(VisitRec) + 2 * (size_t)S * sizeof(int);
 }
 
 template <typename KV, int G, int T, bool PAGED>
@@ -559,10 +685,23 @@ static hipError_t launch_prop_t(const LaunchArgs &a, const TimingHook &hook) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int BH = a.batch * a.num_q_heads;
-    hipLaunchKernelGGL((prop_sample_kernel<KV, T, PAGED>), dim3((unsigned)BH), dim3(kSampleBlock),
-                       prop_sample_lds_bytes(a.kmax, a.S), st, (const KV *)a.v, L, a.seq_lens, a.batch,
-                       a.num_q_heads, G, a.S, max_nt, a.kmax, a.u, a.scale, (const float *)stash,
-                       (const float2 *)stats, a.out, a.sample_idx, a.tile_budget);
+    const size_t lds = prop_sample_lds_bytes(a.kmax, a.S, a.sampler);
+    if (a.sampler == kSamplerSys) {
+        hipLaunchKernelGGL((prop_sample_kernel<KV, T, PAGED, false>), dim3((unsigned)BH), dim3(kSampleBlock), lds,
+                           st, (const KV *)a.v, L, a.seq_lens, a.batch, a.num_q_heads, G, a.S, max_nt, a.kmax,
+                           a.sampler, a.u, a.scale, (const float *)stash, (const float2 *)stats, a.out,
+                           a.sample_idx, a.tile_budget);
+        return hipGetLastError();
+    }
+    if (lds > 64 * 1024) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prop_sample_kernel<KV, T, PAGED, true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((prop_sample_kernel<KV, T, PAGED, true>), dim3((unsigned)BH), dim3(kSampleBlock), lds, st,
+                       (const KV *)a.v, L, a.seq_lens, a.batch, a.num_q_heads, G, a.S, max_nt, a.kmax,
+                       a.sampler, a.u, a.scale, (const float *)stash, (const float2 *)stats, a.out,
+                       a.sample_idx, a.tile_budget);
     return hipGetLastError();
 }
 

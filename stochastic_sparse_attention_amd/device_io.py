@@ -24,6 +24,10 @@ class DeviceInputs:
         import torch
         return torch.from_numpy(self.inp.u(S)).to(self.q.device)
 
+    def uniforms(self, S: int):
+        import torch
+        return torch.from_numpy(self.inp.uniforms(S)).to(self.q.device)
+
 
 def _upload(a: np.ndarray, dtype: str, device):
     import torch

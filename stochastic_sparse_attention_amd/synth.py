@@ -24,6 +24,9 @@ Recipe (every config):
   * U = floor(r * 2^24) * 2^-24 / S with r ~ Unif[0,1): exact in fp32 and in
     [0, 1/S).  One r per (request, q head), or per request where the config
     says so (replicated over that request's heads).
+  * the stratified and i.i.d. threshold generators take S uniforms per
+    (request, q head), on the same 2^-24 grid, from their own generator
+    seeded by (seed, 0x5A17, S).
 """
 from __future__ import annotations
 
@@ -134,6 +137,14 @@ class Inputs:
     def u(self, S: int) -> np.ndarray:
         """Offsets U in [0, 1/S) as fp32 (exact: r is a multiple of 2^-24)."""
         return (self.r / float(S)).astype(np.float32)
+
+    def uniforms(self, S: int) -> np.ndarray:
+        """[B*Hq, S] uniforms in [0, 1) on the 2^-24 grid (exact in fp32), for
+        the stratified and i.i.d. threshold generators; drawn from their own
+        stream, seeded by (seed, S), so the other draws are unchanged."""
+        rng = np.random.default_rng([self.seed, 0x5A17, S])
+        n = self.cfg.batch * self.cfg.num_q_heads
+        return (np.floor(rng.random((n, S)) * 2.0 ** 24) * 2.0 ** -24).astype(np.float32)
 
     @property
     def contiguous(self) -> bool:

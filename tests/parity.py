@@ -25,7 +25,7 @@ def _torch():
     return torch
 
 
-def run_prop(dev, S, T=None):
+def run_prop(dev, S, T=None, sampler="sys"):
     torch = _torch()
     c = dev.inp.cfg
     BH = c.batch * c.num_q_heads
@@ -35,7 +35,11 @@ def run_prop(dev, S, T=None):
     idx = torch.full((BH, S), -7, dtype=torch.int32, device=dev.q.device)
     tb = torch.full((BH, max_nt), -7, dtype=torch.int32, device=dev.q.device)
     import stochastic_sparse_attention_amd as sa
-    sa.santa_decode_prop(dev.problem, dev.q, dev.k, dev.v, S, dev.u(S), out, idx, tb)
+    if sampler == "sys":
+        sa.santa_decode_prop(dev.problem, dev.q, dev.k, dev.v, S, dev.u(S), out, idx, tb)
+    else:
+        sa.santa_decode_prop_sampler(dev.problem, dev.q, dev.k, dev.v, S, sampler, dev.uniforms(S),
+                                     out, idx, tb)
     torch.cuda.synchronize()
     return out.cpu().numpy(), idx.cpu().numpy(), tb.cpu().numpy()
 
@@ -83,14 +87,18 @@ def index_report(gpu_idx, ora_idx, delta):
             "near_edges": int((delta < BOUNDARY_EXEMPT).sum())}
 
 
-def check_prop(dev, S, repeat=True):
-    """Run prop on the GPU and hold it to the bar; returns a report dict."""
+def check_prop(dev, S, repeat=True, sampler="sys"):
+    """Run prop on the GPU (systematic, stratified or i.i.d. thresholds) and
+    hold it to the bar; returns a report dict."""
     inp = dev.inp
     c = inp.cfg
     T = dev.problem.s.tile_len
-    out, idx, tb = run_prop(dev, S)
+    out, idx, tb = run_prop(dev, S, sampler=sampler)
     prob = oracle_problem(dev)
-    r = O.santa_prop(prob, inp.q, inp.k, inp.v, S, inp.u(S))
+    if sampler == "sys":
+        r = O.santa_prop(prob, inp.q, inp.k, inp.v, S, inp.u(S))
+    else:
+        r = O.santa_prop_sampler(prob, inp.q, inp.k, inp.v, S, sampler, inp.uniforms(S))
     rep = index_report(idx, r["idx"], r["delta"])
     assert rep["hard"] == 0, rep
     # budgets: sum to S (or 0 for empty requests), match the GPU's own indices
@@ -116,7 +124,7 @@ def check_prop(dev, S, repeat=True):
     rep["max_abs_vs_replay"] = err
     rep["max_abs_vs_oracle_estimate"] = float(np.max(np.abs(out - r["out"])))
     if repeat:
-        out2, idx2, tb2 = run_prop(dev, S)
+        out2, idx2, tb2 = run_prop(dev, S, sampler=sampler)
         assert np.array_equal(idx, idx2) and np.array_equal(tb, tb2)
         assert np.array_equal(out.view(np.uint32), out2.view(np.uint32))
     return rep

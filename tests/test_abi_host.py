@@ -113,6 +113,20 @@ def test_sample_count_validation(lib):
     assert _flash(lib, _problem(seq_lens=0x2000)) == INVALID   # ragged flash
 
 
+def test_sampler_validation(lib):
+    p = _problem()
+    for bad in (-1, 3, 99):
+        assert lib.santa_decode_prop_sampler(C.byref(p), DUMMY, DUMMY, DUMMY, 128, bad, DUMMY, DUMMY, None,
+                                             None, DUMMY, 1 << 30, None) == INVALID
+    # the sampler call shares the problem and workspace checks of prop
+    assert lib.santa_decode_prop_sampler(C.byref(_problem(tile_len=100)), DUMMY, DUMMY, DUMMY, 128, 1, DUMMY,
+                                         DUMMY, None, None, DUMMY, 1 << 30, None) == INVALID
+    assert lib.santa_decode_prop_sampler(C.byref(p), DUMMY, DUMMY, DUMMY, 128, 2, DUMMY, DUMMY, None, None,
+                                         DUMMY, 10, None) == WORKSPACE
+    assert lib.santa_decode_prop_sampler(C.byref(_problem(batch=0)), DUMMY, DUMMY, DUMMY, 128, 1, DUMMY,
+                                         DUMMY, None, None, DUMMY, 1 << 30, None) == OK
+
+
 def test_pointer_and_workspace_validation(lib):
     p = _problem()
     need = _wsize(lib, p, PROP, 128)[1]
@@ -142,7 +156,7 @@ def test_empty_batch_is_a_noop(lib):
 def test_status_strings_and_version(lib):
     for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 12):
         assert isinstance(_lib.status_string(code), str) and _lib.status_string(code)
-    assert lib.santa_abi_version() >= 1
+    assert lib.santa_abi_version() >= 2
     assert lib.santa_set_timing_events(None, None) == OK
 
 

@@ -61,6 +61,31 @@ def test_prop_many_tiles(gpu, T, n):
     _say("T", T, "n", n, rep)
 
 
+@pytest.mark.parametrize("sampler", ["strat", "iid"])
+@pytest.mark.parametrize("S", [1, 96, 128, 1000, 4096])
+def test_prop_samplers(gpu, sampler, S):
+    """Stratified and i.i.d. thresholds (key design 1) through the same
+    schedule: S = 1, non-powers of two, and S = 4096 (an i.i.d. threshold list
+    above 64 KiB of LDS)."""
+    import parity
+    cfg = synth.small_config(2, batch=2, seq_len=3000, num_q_heads=8, num_kv_heads=2)
+    rep = parity.check_prop(_dev(cfg, 8, gpu), S, sampler=sampler)
+    _say(sampler, "S", S, rep)
+
+
+@pytest.mark.parametrize("sampler", ["strat", "iid"])
+def test_prop_samplers_ragged_paged_many_tiles(gpu, sampler):
+    """Mixed lengths with paged KV, and a long sequence that takes the LDS
+    reducer (313 tiles), for both list generators."""
+    import parity
+    cfg = synth.small_config(5, batch=5, seq_len=4000, min_seq_len=100)
+    rep = parity.check_prop(_dev(cfg, 9, gpu), 128, sampler=sampler)
+    _say(sampler, "paged ragged", rep)
+    cfg = synth.small_config(2, batch=1, seq_len=20000, num_q_heads=8, num_kv_heads=2)
+    rep = parity.check_prop(_dev(cfg, 10, gpu, tile_len=64), 256, sampler=sampler)
+    _say(sampler, "313 tiles", rep)
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (32, 8), (16, 2)])
 def test_prop_gqa_groups(gpu, hq, hkv):
     import parity
