@@ -220,6 +220,8 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-exact", action="store_true")
+    ap.add_argument("--no-samplers", action="store_true",
+                    help="skip timing prop with the stratified and i.i.d. threshold generators")
     ap.add_argument("--no-flash", action="store_true",
                     help="skip the S2ANTA-flash leg (run where the workload has a flash budget)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -360,6 +362,17 @@ def main(argv=None):
             "partial_kernel_GB/s": round(eb["partial"] / (np.mean(ekern) * 1e-3) / 1e9, 1),
         }
         result["speedup_vs_exact"] = round(ems / ms, 3)
+
+    if not args.no_samplers:
+        uu = dev.uniforms(S)
+        result["samplers"] = {"sys": {"us_per_step": round(ms_eager * 1e3, 3)}}
+        for smp in ("strat", "iid"):
+            def smp_step(i, smp=smp):
+                c = i % ncopy
+                sa.santa_decode_prop_sampler(dev.problem, dev.q, ks[c], vs[c], S, smp, uu, out, workspace=ws)
+            sms, _sk = time_steps(smp_step, args.steps, args.warmup)
+            log(f"bench: prop with {smp} thresholds {sms * 1e3:.2f} us/step (eager)")
+            result["samplers"][smp] = {"us_per_step": round(sms * 1e3, 3)}
 
     if cfg.S_flash and not args.no_flash:
         Sf = cfg.S_flash
