@@ -312,7 +312,7 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: S2ANTA-prop", "batch": cfg.batch,
+        "config": {"workload": f"{cfg.name}: S2ANTA-prop", "batch": cfg.batch, "kv_dtype": cfg.kv_dtype,
                    "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads,
                    "head_dim": cfg.head_dim, "seq_len": cfg.seq_len, "S": S, "tile_len": T,
                    "kv_copies_rotated": ncopy},

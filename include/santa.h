@@ -58,7 +58,11 @@ typedef enum {
     SANTA_ERR_HIP = -4           /* a HIP launch reported an error                    */
 } santa_status;
 
-typedef enum { SANTA_F32 = 0, SANTA_BF16 = 1 } santa_dtype;
+/* Storage types.  SANTA_FP8_E4M3 is OCP e4m3 (1 sign, 4 exponent bits with
+   bias 7, 3 mantissa bits, no infinities; 0x7F/0xFF are NaN), for K and V
+   only: with it, q is bf16.  Every e4m3 value is exact in bf16, and the
+   kernels widen K to bf16 before scoring and V to fp32 before summing. */
+typedef enum { SANTA_F32 = 0, SANTA_BF16 = 1, SANTA_FP8_E4M3 = 2 } santa_dtype;
 
 typedef enum {
     SANTA_VARIANT_PROP = 0,
@@ -78,7 +82,8 @@ typedef struct {
                                  that request empty: its output rows are 0, its
                                  sample indices -1 and its budgets 0.  Values
                                  above max_seq_len are clamped to it.              */
-    int32_t q_dtype;          /* santa_dtype; must equal kv_dtype                  */
+    int32_t q_dtype;          /* santa_dtype; equal to kv_dtype, or SANTA_BF16
+                                 when kv_dtype is SANTA_FP8_E4M3                   */
     int32_t kv_dtype;         /* santa_dtype                                       */
     int32_t page_size;        /* 0: contiguous K/V.  Else a multiple of 16: paged
                                  pools                                             */

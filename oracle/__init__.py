@@ -34,12 +34,16 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 
+# storage formats of the oracle's problem struct
+FORMATS = {"f32": 0, "bf16": 1, "fp8": 2}
+
+
 class _Problem(C.Structure):
     _fields_ = [
         ("batch", C.c_int), ("num_q_heads", C.c_int), ("num_kv_heads", C.c_int),
         ("head_dim", C.c_int), ("max_seq_len", C.c_int),
         ("seq_lens", C.POINTER(C.c_int)),
-        ("q_bf16", C.c_int), ("kv_bf16", C.c_int),
+        ("q_fmt", C.c_int), ("kv_fmt", C.c_int),
         ("page_size", C.c_int), ("page_table", C.POINTER(C.c_int)),
         ("max_pages", C.c_int), ("scale", C.c_float), ("tile_len", C.c_int),
     ]
@@ -94,12 +98,12 @@ class Problem:
     """
 
     def __init__(self, batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, *,
-                 q_bf16, kv_bf16, scale, tile_len, seq_lens=None, page_size=0,
+                 q_dtype, kv_dtype, scale, tile_len, seq_lens=None, page_size=0,
                  page_table=None):
         self._seq = None if seq_lens is None else np.ascontiguousarray(seq_lens, np.int32)
         self._pt = None if page_table is None else np.ascontiguousarray(page_table, np.int32)
         self.s = _Problem(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
-                          _iptr(self._seq), int(q_bf16), int(kv_bf16), page_size,
+                          _iptr(self._seq), FORMATS[q_dtype], FORMATS[kv_dtype], page_size,
                           _iptr(self._pt), 0 if self._pt is None else self._pt.shape[1],
                           float(np.float32(scale)), tile_len)
         self.batch, self.num_q_heads, self.head_dim = batch, num_q_heads, head_dim
@@ -113,7 +117,7 @@ class Problem:
         paged = c.page_size > 0
         ragged = paged or not inp.uniform_len
         return cls(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim, c.seq_len,
-                   q_bf16=c.q_dtype == "bf16", kv_bf16=c.kv_dtype == "bf16",
+                   q_dtype=c.q_dtype, kv_dtype=c.kv_dtype,
                    scale=inp.scale, tile_len=tile_len or c.tile_len,
                    seq_lens=inp.seq_lens if ragged else None, page_size=c.page_size,
                    page_table=inp.page_table if paged else None)

@@ -53,7 +53,8 @@ typedef struct {
     int batch, num_q_heads, num_kv_heads, head_dim;
     int max_seq_len;          /* contiguous: KV rows per (b, kv head)       */
     const int *seq_lens;      /* host [batch] or NULL (all = max_seq_len)   */
-    int q_bf16, kv_bf16;      /* 1: values are bf16 bit patterns (uint16)   */
+    int q_fmt, kv_fmt;        /* storage: 0 fp32, 1 bf16 bit patterns        */
+                              /* (uint16), 2 OCP e4m3 bytes (uint8)          */
     int page_size;            /* 0: contiguous [B,Hkv,max_seq_len,d]        */
     const int *page_table;    /* host [batch, max_pages] (paged only)       */
     int max_pages;
@@ -70,10 +71,23 @@ static double widen_bf16(uint16_t bits)
     return (double)f;
 }
 
-static double load_val(const void *base, size_t i, int is_bf16)
+/* OCP e4m3 (the 8-bit float of the OCP FP8 formats): sign, a 4-bit
+   exponent with bias 7, a 3-bit mantissa; exponent field 0 holds the
+   subnormals m/8 * 2^-6, and S.1111.111 is NaN (there are no infinities). */
+static double widen_e4m3(uint8_t bits)
 {
-    if (is_bf16)
+    int sign = bits >> 7, e = (bits >> 3) & 15, m = bits & 7;
+    if (e == 15 && m == 7) return NAN;
+    double mag = (e == 0) ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+static double load_val(const void *base, size_t i, int fmt)
+{
+    if (fmt == 1)
         return widen_bf16(((const uint16_t *)base)[i]);
+    if (fmt == 2)
+        return widen_e4m3(((const uint8_t *)base)[i]);
     return (double)((const float *)base)[i];
 }
 
@@ -109,7 +123,7 @@ void oracle_logits(const oracle_problem *p, const void *q, const void *k,
         size_t koff = kv_row_offset(p, b, g, j);
         double dot = 0.0;
         for (int i = 0; i < d; ++i)
-            dot += load_val(q, qoff + i, p->q_bf16) * load_val(k, koff + i, p->kv_bf16);
+            dot += load_val(q, qoff + i, p->q_fmt) * load_val(k, koff + i, p->kv_fmt);
         x[j] = (double)p->scale * dot;
     }
 }
@@ -213,7 +227,7 @@ static void mean_of_rows(const oracle_problem *p, const void *v, int b, int g,
     for (int i = 0; i < d; ++i) out[i] = 0.0;
     for (int m = 0; m < count; ++m) {
         size_t off = kv_row_offset(p, b, g, idx[m]);
-        for (int i = 0; i < d; ++i) out[i] += load_val(v, off + i, p->kv_bf16);
+        for (int i = 0; i < d; ++i) out[i] += load_val(v, off + i, p->kv_fmt);
     }
     for (int i = 0; i < d; ++i) out[i] /= (double)count;
 }
@@ -429,7 +443,7 @@ int oracle_exact(const oracle_problem *p, const void *q, const void *k,
         for (int j = 0; j < n; ++j) {
             double a = e[j] / Z;
             size_t off = kv_row_offset(p, b, g, j);
-            for (int i = 0; i < d; ++i) o[i] += a * load_val(v, off + i, p->kv_bf16);
+            for (int i = 0; i < d; ++i) o[i] += a * load_val(v, off + i, p->kv_fmt);
         }
         free(x); free(e);
     }

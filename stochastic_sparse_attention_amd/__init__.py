@@ -12,7 +12,7 @@ from __future__ import annotations
 import ctypes as C
 
 from . import _lib
-from ._lib import SantaError, santa_problem, SANTA_F32, SANTA_BF16, VARIANT, SAMPLER
+from ._lib import SantaError, santa_problem, SANTA_F32, SANTA_BF16, SANTA_FP8_E4M3, VARIANT, SAMPLER
 
 __all__ = [
     "Problem", "santa_workspace_size", "santa_decode_prop", "santa_decode_prop_sampler", "santa_decode_flash",
@@ -35,14 +35,17 @@ class Problem:
     """santa_problem plus the device tensors it points to (kept alive)."""
 
     def __init__(self, batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, *, dtype,
-                 scale, tile_len, seq_lens=None, page_size=0, page_table=None):
-        dt = {"f32": SANTA_F32, "bf16": SANTA_BF16}[dtype]
+                 scale, tile_len, seq_lens=None, page_size=0, page_table=None, kv_dtype=None):
+        """dtype: storage of q ("f32" or "bf16"); kv_dtype: storage of K and V
+        (default: dtype; "fp8" is OCP e4m3 with bf16 q)."""
+        codes = {"f32": SANTA_F32, "bf16": SANTA_BF16, "fp8": SANTA_FP8_E4M3}
+        dt, kdt = codes[dtype], codes[kv_dtype or dtype]
         self.seq_lens = seq_lens
         self.page_table = page_table
         max_pages = 0 if page_table is None else int(page_table.shape[1])
         self.s = santa_problem(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
                                None if seq_lens is None else seq_lens.data_ptr(),
-                               dt, dt, page_size,
+                               dt, kdt, page_size,
                                None if page_table is None else page_table.data_ptr(),
                                max_pages, float(scale), tile_len)
 

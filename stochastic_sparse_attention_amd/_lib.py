@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("SANTA_LIB") or os.path.join(HERE, "libsanta.so")
 
 SANTA_OK, SANTA_ERR_INVALID, SANTA_ERR_UNSUPPORTED, SANTA_ERR_WORKSPACE, SANTA_ERR_HIP = 0, -1, -2, -3, -4
-SANTA_F32, SANTA_BF16 = 0, 1
+SANTA_F32, SANTA_BF16, SANTA_FP8_E4M3 = 0, 1, 2
 VARIANT = {"prop": 0, "flash": 1, "exact": 2}
 SAMPLER = {"sys": 0, "strat": 1, "iid": 2}
 

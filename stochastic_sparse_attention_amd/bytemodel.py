@@ -21,7 +21,7 @@ F32 = 4
 
 
 def elem_bytes(dtype: str) -> int:
-    return 2 if dtype == "bf16" else 4
+    return {"bf16": 2, "fp8": 1, "f32": 4}[dtype]
 
 
 def _lens(cfg, seq_lens=None):

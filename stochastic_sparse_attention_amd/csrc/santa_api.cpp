@@ -38,7 +38,8 @@ int validate(const santa_problem *p, int variant, int S, Derived *d) {
     if (p->num_q_heads % p->num_kv_heads) return SANTA_ERR_INVALID;
     if (p->tile_len % 64) return SANTA_ERR_INVALID;
     if (p->q_dtype != SANTA_F32 && p->q_dtype != SANTA_BF16) return SANTA_ERR_INVALID;
-    if (p->kv_dtype != SANTA_F32 && p->kv_dtype != SANTA_BF16) return SANTA_ERR_INVALID;
+    if (p->kv_dtype != SANTA_F32 && p->kv_dtype != SANTA_BF16 && p->kv_dtype != SANTA_FP8_E4M3)
+        return SANTA_ERR_INVALID;
     if (!(p->scale > 0.0f) || p->scale != p->scale) return SANTA_ERR_INVALID;
     if (p->page_size < 0) return SANTA_ERR_INVALID;
     if (p->page_size > 0) {
@@ -49,7 +50,10 @@ int validate(const santa_problem *p, int variant, int S, Derived *d) {
     }
     const int G = p->num_q_heads / p->num_kv_heads;
     if (p->head_dim != kHeadDimBuilt) return SANTA_ERR_UNSUPPORTED;
-    if (p->q_dtype != p->kv_dtype) return SANTA_ERR_UNSUPPORTED;
+    // built pairs: fp32/fp32, bf16/bf16 and bf16 queries with e4m3 KV
+    const bool pair_built = p->q_dtype == p->kv_dtype ||
+                            (p->q_dtype == SANTA_BF16 && p->kv_dtype == SANTA_FP8_E4M3);
+    if (!pair_built) return SANTA_ERR_UNSUPPORTED;
     if (!(G == 1 || G == 2 || G == 4 || G == 8)) return SANTA_ERR_UNSUPPORTED;
     if (!tile_len_built(p->tile_len)) return SANTA_ERR_UNSUPPORTED;
     const long nt = ((long)p->max_seq_len + p->tile_len - 1) / p->tile_len;
@@ -120,7 +124,7 @@ santa::LaunchArgs make_args(const santa_problem *p, const Derived &d, const void
     a.page_size = p->page_size;
     a.page_table = p->page_table;
     a.max_pages = p->max_pages_per_seq;
-    a.bf16 = p->kv_dtype == SANTA_BF16;
+    a.kv_dtype = p->kv_dtype;
     a.scale = p->scale;
     a.q = q;
     a.k = k;

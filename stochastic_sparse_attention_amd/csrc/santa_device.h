@@ -59,6 +59,33 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                            __builtin_bit_cast(bf16x2_t, b), acc, false);
 }
 
+// ---------------------------------------------------------------- fp8
+// OCP e4m3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+// infinities).  The gfx950 conversion decodes it exactly, and every e4m3
+// value is exact in bf16, so widening to bf16 keeps the value.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// bf16 pair (lo, hi) from two exactly representable floats: their high halves
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+// two e4m3 bytes (the low or the high half of w) -> a bf16 pair
+template <bool HIGH>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16(uint32_t w) {
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HIGH);
+    return pack_bf16_exact(a.x, a.y);
+}
+// four e4m3 bytes -> four floats
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float *f) {
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y;
+}
+
+// storage type of the query for a KV storage type: fp8 KV keeps bf16 queries
+template <typename KV> struct QOf { typedef KV type; };
+template <> struct QOf<uint8_t> { typedef uint16_t type; };
+
 // ---------------------------------------------------------------- DPP
 // quad_perm control words
 constexpr int kQuadXor1 = 0xB1;   // [1,0,3,2]

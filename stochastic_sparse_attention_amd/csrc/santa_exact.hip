@@ -25,7 +25,7 @@ namespace santa {
 // ===================================================================
 template <typename KV, int G, int T, bool PAGED>
 __global__ __launch_bounds__(kBlock) void exact_partial_kernel(
-    const KV *__restrict__ q, const KV *__restrict__ k, const KV *__restrict__ v, KVLayout L,
+    const typename QOf<KV>::type *__restrict__ q, const KV *__restrict__ k, const KV *__restrict__ v, KVLayout L,
     const int *__restrict__ seq_lens, int num_q_heads, int max_nt, float scale,
     float *__restrict__ part_m, float *__restrict__ part_l, float *__restrict__ part_o) {
     typedef typename ScorerFor<KV, G, T, PAGED>::type SC;
@@ -163,11 +163,11 @@ static hipError_t launch_exact_t(const LaunchArgs &a, const TimingHook &hook) {
     // they bracket the kernel's execution and nothing else
     if (hook.begin)
         hipExtLaunchKernelGGL((exact_partial_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * max_nt)), dim3(kBlock), 0, st, (hipEvent_t)hook.begin, (hipEvent_t)hook.end, 0,
-                       (const KV *)a.q, (const KV *)a.k, (const KV *)a.v, L, a.seq_lens, a.num_q_heads,
+                       (const typename QOf<KV>::type *)a.q, (const KV *)a.k, (const KV *)a.v, L, a.seq_lens, a.num_q_heads,
                        max_nt, a.scale, (float *)a.ws.part_m, (float *)a.ws.part_l, (float *)a.ws.part_o);
     else
         hipLaunchKernelGGL((exact_partial_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * max_nt)), dim3(kBlock), 0, st,
-                       (const KV *)a.q, (const KV *)a.k, (const KV *)a.v, L, a.seq_lens, a.num_q_heads,
+                       (const typename QOf<KV>::type *)a.q, (const KV *)a.k, (const KV *)a.v, L, a.seq_lens, a.num_q_heads,
                        max_nt, a.scale, (float *)a.ws.part_m, (float *)a.ws.part_l, (float *)a.ws.part_o);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

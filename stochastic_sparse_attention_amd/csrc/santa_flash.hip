@@ -34,7 +34,7 @@ namespace santa {
 // nonzero weight on).
 template <typename KV, int G, int T, bool PAGED>
 __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
-    const KV *__restrict__ q, const KV *__restrict__ k, const KV *__restrict__ v, KVLayout L,
+    const typename QOf<KV>::type *__restrict__ q, const KV *__restrict__ k, const KV *__restrict__ v, KVLayout L,
     int num_q_heads, int nt, int Sf, int S, float scale, const float *__restrict__ u,
     float *__restrict__ part_m, float *__restrict__ part_z, float *__restrict__ part_o,
     int *__restrict__ sample_idx) {
@@ -170,12 +170,12 @@ static hipError_t launch_flash_t(const LaunchArgs &a, const TimingHook &hook) {
     // they bracket the kernel's execution and nothing else
     if (hook.begin)
         hipExtLaunchKernelGGL((flash_tile_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * nt)), dim3(kBlock), 0, st, (hipEvent_t)hook.begin, (hipEvent_t)hook.end, 0,
-                       (const KV *)a.q, (const KV *)a.k, (const KV *)a.v, L, a.num_q_heads, nt, a.S / nt,
+                       (const typename QOf<KV>::type *)a.q, (const KV *)a.k, (const KV *)a.v, L, a.num_q_heads, nt, a.S / nt,
                        a.S, a.scale, a.u, (float *)a.ws.part_m, (float *)a.ws.part_l, (float *)a.ws.part_o,
                        a.sample_idx);
     else
         hipLaunchKernelGGL((flash_tile_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * nt)), dim3(kBlock), 0, st,
-                       (const KV *)a.q, (const KV *)a.k, (const KV *)a.v, L, a.num_q_heads, nt, a.S / nt,
+                       (const typename QOf<KV>::type *)a.q, (const KV *)a.k, (const KV *)a.v, L, a.num_q_heads, nt, a.S / nt,
                        a.S, a.scale, a.u, (float *)a.ws.part_m, (float *)a.ws.part_l, (float *)a.ws.part_o,
                        a.sample_idx);
     hipError_t e = hipGetLastError();

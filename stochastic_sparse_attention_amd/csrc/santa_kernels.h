@@ -126,6 +126,12 @@ __device__ __forceinline__ void load_v8<uint16_t>(const uint16_t *p, float (&v)[
     v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
 }
 template <>
+__device__ __forceinline__ void load_v8<uint8_t>(const uint8_t *p, float (&v)[8]) {
+    const uint2 a = *reinterpret_cast<const uint2 *>(p);
+    e4m3x4_to_f32(a.x, v);
+    e4m3x4_to_f32(a.y, v + 4);
+}
+template <>
 __device__ __forceinline__ void load_v8<float>(const float *p, float (&v)[8]) {
     const u32x4 a = reinterpret_cast<const u32x4 *>(p)[0];
     const u32x4 c = reinterpret_cast<const u32x4 *>(p)[1];
@@ -140,13 +146,22 @@ __device__ __forceinline__ void load_v8<float>(const float *p, float (&v)[8]) {
 template <typename KV> struct Raw8;
 template <> struct Raw8<uint16_t> { u32x4 x[1]; };
 template <> struct Raw8<float> { u32x4 x[2]; };
+template <> struct Raw8<uint8_t> { uint2 x; };
 
 template <typename KV>
 __device__ __forceinline__ Raw8<KV> load_raw8(const KV *p) {
     Raw8<KV> r;
+    if constexpr (sizeof(KV) == 1) {
+        r.x = *reinterpret_cast<const uint2 *>(p);
+    } else {
 #pragma unroll
-    for (int i = 0; i < (int)(sizeof(r.x) / sizeof(u32x4)); ++i) r.x[i] = reinterpret_cast<const u32x4 *>(p)[i];
+        for (int i = 0; i < (int)(sizeof(r.x) / sizeof(u32x4)); ++i) r.x[i] = reinterpret_cast<const u32x4 *>(p)[i];
+    }
     return r;
+}
+__device__ __forceinline__ void widen8(const Raw8<uint8_t> &r, float (&v)[8]) {
+    e4m3x4_to_f32(r.x.x, v);
+    e4m3x4_to_f32(r.x.y, v + 4);
 }
 __device__ __forceinline__ void widen8(const Raw8<uint16_t> &r, float (&v)[8]) {
     const u32x4 a = r.x[0];
@@ -250,7 +265,8 @@ inline KVLayout layout_of(const LaunchArgs &a) {
         default: return hipErrorInvalidValue;           \
     }
 #define SANTA_DISPATCH(FN)                                          \
-    if (a.bf16) { SANTA_G_CASES(uint16_t, FN) }                     \
+    if (a.kv_dtype == kKvBf16) { SANTA_G_CASES(uint16_t, FN) }      \
+    else if (a.kv_dtype == kKvFp8) { SANTA_G_CASES(uint8_t, FN) }   \
     else { SANTA_G_CASES(float, FN) }
 
 }  // namespace santa

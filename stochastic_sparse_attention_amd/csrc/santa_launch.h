@@ -9,6 +9,9 @@
 
 namespace santa {
 
+// KV storage types (the values of santa_dtype)
+constexpr int kKvF32 = 0, kKvBf16 = 1, kKvFp8 = 2;
+
 // threshold generators of prop (the values of santa_sampler)
 constexpr int kSamplerSys = 0, kSamplerStrat = 1, kSamplerIid = 2;
 
@@ -37,7 +40,7 @@ struct LaunchArgs {
     int page_size;
     const int *page_table;
     int max_pages;
-    int bf16;
+    int kv_dtype;   // kKvF32 / kKvBf16 / kKvFp8 (q is bf16 for fp8 KV)
     float scale;
     const void *q, *k, *v;
     int S;

@@ -29,7 +29,7 @@ namespace santa {
 // stats [B, Hq, max_nt] float2: (m_t unscaled tile max, Z_t = sum_j e_j)
 template <typename KV, int G, int T, bool PAGED>
 __global__ __launch_bounds__(kBlock) void prop_pass1_kernel(
-    const KV *__restrict__ q, const KV *__restrict__ k, KVLayout L, const int *__restrict__ seq_lens,
+    const typename QOf<KV>::type *__restrict__ q, const KV *__restrict__ k, KVLayout L, const int *__restrict__ seq_lens,
     int num_q_heads, int max_nt, float scale, float *__restrict__ stash, float2 *__restrict__ stats) {
     typedef typename ScorerFor<KV, G, T, PAGED>::type SC;
     typedef typename SC::acc_t acc_t;
@@ -676,11 +676,11 @@ static hipError_t launch_prop_t(const LaunchArgs &a, const TimingHook &hook) {
     // they bracket the kernel's execution and nothing else
     if (hook.begin)
         hipExtLaunchKernelGGL((prop_pass1_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * max_nt)), dim3(kBlock), 0, st, (hipEvent_t)hook.begin, (hipEvent_t)hook.end, 0,
-                       (const KV *)a.q, (const KV *)a.k, L, a.seq_lens, a.num_q_heads, max_nt, a.scale,
+                       (const typename QOf<KV>::type *)a.q, (const KV *)a.k, L, a.seq_lens, a.num_q_heads, max_nt, a.scale,
                        stash, stats);
     else
         hipLaunchKernelGGL((prop_pass1_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * max_nt)), dim3(kBlock), 0, st,
-                       (const KV *)a.q, (const KV *)a.k, L, a.seq_lens, a.num_q_heads, max_nt, a.scale,
+                       (const typename QOf<KV>::type *)a.q, (const KV *)a.k, L, a.seq_lens, a.num_q_heads, max_nt, a.scale,
                        stash, stats);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -59,7 +59,9 @@ __device__ __forceinline__ size_t block_base(const KVLayout &L, int b, int g, in
 }
 
 // ------------------------------------------------------------------ MFMA
-template <int G, int T, bool PAGED>
+// KV: uint16_t (bf16 rows of 256 bytes) or uint8_t (e4m3 rows of 128 bytes,
+// widened to bf16 on their way into LDS)
+template <typename KV, int G, int T, bool PAGED>
 struct ScorerMfma {
     typedef float acc_t;
     static constexpr int NS = T / 64;
@@ -87,13 +89,19 @@ struct ScorerMfma {
                 bf16x8_t, *reinterpret_cast<const u32x4 *>(q_group + hsrc * kHeadDim + 32 * kb + 8 * kq));
     }
 
-    // K is read 4 whole rows (4 x 256 bytes) per load instruction: lane l
-    // holds 16-byte piece l%16 of row 4 kb + l/16 of the wave's 16-row block.
-    // The block then goes through the wave's 4 KiB of `stage` (piece p of row
-    // r at slot p ^ r, so that both the row-wise writes and the token-wise
-    // reads touch every bank once) into the MFMA layout: lane l reads piece
-    // 4 kb + l/16 of token l%16.
-    __device__ __forceinline__ void score(const uint16_t *__restrict__ k, const KVLayout &L, int b, int g,
+    // K is read as whole rows: bf16, 4 rows (4 x 256 bytes) per load
+    // instruction, lane l holding 16-byte piece l%16 of row 4 kb + l/16 of the
+    // wave's 16-row block; e4m3, 8 rows (8 x 128 bytes) per instruction, lane
+    // l holding bytes 16 (l%8) .. 16 (l%8) + 15 of row 8 i + l/8, which widen
+    // to bf16 pieces 2 (l%8) and 2 (l%8) + 1.  The block then goes through
+    // the wave's 4 KiB of `stage` as bf16 (piece p of row r at slot p ^ r,
+    // so that both the row-wise writes and the token-wise reads touch every
+    // bank once) into the MFMA layout: lane l reads piece 4 kb + l/16 of
+    // token l%16.
+    static constexpr bool kFp8 = sizeof(KV) == 1;
+    static constexpr int kLoads = kFp8 ? 2 : 4;     // 16-byte loads per lane per 16-row block
+
+    __device__ __forceinline__ void score(const KV *__restrict__ k, const KVLayout &L, int b, int g,
                                           int t0, int n, u32x4 *stage) {
         const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
         const int tok = lane & 15, kq = lane >> 4;
@@ -103,26 +111,38 @@ struct ScorerMfma {
             size_t base[CH];
 #pragma unroll
             for (int ii = 0; ii < CH; ++ii) base[ii] = block_base<PAGED>(L, b, g, t0 + 64 * (s0 + ii) + 16 * w, n, t0);
-            u32x4 kv[CH][4];
+            u32x4 kv[CH][kLoads];
 #pragma unroll
             for (int ii = 0; ii < CH; ++ii) {
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
+                for (int li = 0; li < kLoads; ++li) {
                     // rows past the end read the block's row 0 (always a valid
                     // row of the tile); their scores are masked below
-                    const int r = 4 * kb + kq;
+                    const int r = kFp8 ? 8 * li + (lane >> 3) : 4 * li + kq;
+                    const int piece = kFp8 ? (lane & 7) : tok;
                     const bool valid = t0 + 64 * (s0 + ii) + 16 * w + r < n;
                     const u32x4 *rowp =
-                        reinterpret_cast<const u32x4 *>(k + base[ii] + (size_t)(valid ? r : 0) * kHeadDim) + tok;
-                    kv[ii][kb] = __builtin_nontemporal_load(rowp);
+                        reinterpret_cast<const u32x4 *>(k + base[ii] + (size_t)(valid ? r : 0) * kHeadDim) + piece;
+                    kv[ii][li] = __builtin_nontemporal_load(rowp);
                 }
             }
 #pragma unroll
             for (int ii = 0; ii < CH; ++ii) {
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    const int r = 4 * kb + kq;
-                    wst[r * 16 + (tok ^ r)] = kv[ii][kb];
+                for (int li = 0; li < kLoads; ++li) {
+                    if constexpr (kFp8) {
+                        const int r = 8 * li + (lane >> 3), p8 = lane & 7;
+                        const u32x4 raw = kv[ii][li];
+                        const u32x4 lo = {e4m3x2_to_bf16<false>(raw.x), e4m3x2_to_bf16<true>(raw.x),
+                                          e4m3x2_to_bf16<false>(raw.y), e4m3x2_to_bf16<true>(raw.y)};
+                        const u32x4 hi = {e4m3x2_to_bf16<false>(raw.z), e4m3x2_to_bf16<true>(raw.z),
+                                          e4m3x2_to_bf16<false>(raw.w), e4m3x2_to_bf16<true>(raw.w)};
+                        wst[r * 16 + ((2 * p8) ^ r)] = lo;
+                        wst[r * 16 + ((2 * p8 + 1) ^ r)] = hi;
+                    } else {
+                        const int r = 4 * li + kq;
+                        wst[r * 16 + (tok ^ r)] = kv[ii][li];
+                    }
                 }
                 wave_sync_lds();
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -222,7 +242,7 @@ struct ScorerValu {
     }
 };
 
-// scorer used for a storage type: MFMA for bf16, VALU/fp64 for fp32
+// scorer used for a storage type: MFMA for bf16 and e4m3, VALU/fp64 for fp32
 template <typename KV, int G, int T, bool PAGED> struct ScorerFor;
 template <int G, int T, bool PAGED> struct ScorerFor<float, G, T, PAGED> {
     typedef ScorerValu<float, G, T, PAGED> type;
@@ -233,9 +253,12 @@ template <int G, int T, bool PAGED> struct ScorerFor<uint16_t, G, T, PAGED> {
 };
 #else
 template <int G, int T, bool PAGED> struct ScorerFor<uint16_t, G, T, PAGED> {
-    typedef ScorerMfma<G, T, PAGED> type;
+    typedef ScorerMfma<uint16_t, G, T, PAGED> type;
 };
 #endif
+template <int G, int T, bool PAGED> struct ScorerFor<uint8_t, G, T, PAGED> {
+    typedef ScorerMfma<uint8_t, G, T, PAGED> type;
+};
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 

@@ -49,6 +49,6 @@ def to_device(inp: Inputs, device="cuda", tile_len=None, seq_lens=None) -> Devic
     sl = torch.from_numpy(np.ascontiguousarray(lens, np.int32)).to(device) if ragged else None
     pt = torch.from_numpy(inp.page_table).to(device) if paged else None
     prob = Problem(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim, c.seq_len,
-                   dtype=c.kv_dtype, scale=float(inp.scale), tile_len=tile_len or c.tile_len,
+                   dtype=c.q_dtype, kv_dtype=c.kv_dtype, scale=float(inp.scale), tile_len=tile_len or c.tile_len,
                    seq_lens=sl, page_size=c.page_size, page_table=pt)
     return DeviceInputs(inp, prob, q, k, v, sl, pt)

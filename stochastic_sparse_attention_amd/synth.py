@@ -50,6 +50,7 @@ class Config:
     head_dim: int
     seq_len: int                  # n_k (contiguous) or the maximum (mixed batch)
     q_dtype: str                  # "f32" | "bf16"
+                                  # kv_dtype also "fp8" (OCP e4m3, with bf16 q)
     kv_dtype: str
     S: int                        # samples per q head (prop)
     tile_len: int                 # T, tokens per tile
@@ -89,6 +90,12 @@ CONFIGS = {
     5: Config(5, "Qwen3-8B-shaped mixed batch of 64, paged 16", 64, 32, 8, 128, 32768,
               "bf16", "bf16", S=128, tile_len=256, page_size=16, min_seq_len=4096,
               density=(0.001, 0.05), variants=("prop", "exact")),
+    # e4m3 KV (bf16 queries): the 32k layer shape again, at batch 1 and 16
+    6: Config(6, "Llama-3.1-8B decode layer, 32k context, batch 1, fp8 e4m3 KV", 1, 32, 8, 128, 32768,
+              "bf16", "fp8", S=128, tile_len=256, hot=64, sinks=4, variants=("prop", "exact")),
+    7: Config(7, "Llama-3.1-8B decode layer, 32k context, batch 16, fp8 e4m3 KV", 16, 32, 8, 128, 32768,
+              "bf16", "fp8", S=128, tile_len=256, hot=64, sinks=4, S_flash=2048, u_per_request=True,
+              variants=("prop", "flash", "exact")),
 }
 
 
@@ -118,6 +125,42 @@ def f32_to_bf16_bits(x: np.ndarray, chunk: int = 1 << 24) -> np.ndarray:
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# OCP e4m3 storage helpers (1 sign bit, 4 exponent bits with bias 7, 3
+# mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6; S.1111.111
+# is NaN; no infinities; largest finite magnitude 448)
+# --------------------------------------------------------------------------
+def _e4m3_magnitudes() -> np.ndarray:
+    """Values of the codes 0..126 (non-negative, finite), increasing."""
+    c = np.arange(127)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round to e4m3: nearest, ties to the even code (even mantissa),
+    magnitudes above 448 saturate to 448; NaN maps to 0x7F."""
+    x = np.asarray(x, np.float32)
+    a = np.abs(x.astype(np.float64)).reshape(-1)
+    mags = _e4m3_magnitudes()
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(take_hi, hi, lo).astype(np.uint8)
+    code[a >= 448.0] = 126
+    code |= (np.signbit(x.reshape(-1)).astype(np.uint8) << 7)
+    code[np.isnan(a)] = 0x7F
+    return code.reshape(x.shape)
+
+
+def e4m3_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(b, np.uint8)
+    table = np.concatenate([_e4m3_magnitudes(), [np.nan]])
+    mag = table[b & 0x7F]
+    return np.where(b & 0x80, -mag, mag).astype(np.float32)
 
 
 @dataclass
@@ -158,15 +201,23 @@ class Inputs:
         """fp32 view of a stored tensor (widens bf16 exactly)."""
         a = getattr(self, name)
         dt = self.cfg.q_dtype if name == "q" else self.cfg.kv_dtype
-        return bf16_bits_to_f32(a) if dt == "bf16" else a
+        return _stored_f32(a, dt)
 
 
 def _store(x: np.ndarray, dtype: str) -> np.ndarray:
-    return f32_to_bf16_bits(x) if dtype == "bf16" else np.ascontiguousarray(x, np.float32)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "fp8":
+        return f32_to_e4m3_bits(x)
+    return np.ascontiguousarray(x, np.float32)
 
 
 def _stored_f32(x: np.ndarray, dtype: str) -> np.ndarray:
-    return bf16_bits_to_f32(x) if dtype == "bf16" else x
+    if dtype == "bf16":
+        return bf16_bits_to_f32(x)
+    if dtype == "fp8":
+        return e4m3_bits_to_f32(x)
+    return x
 
 
 def make_inputs(cfg: Config, seed: int) -> Inputs:

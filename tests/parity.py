@@ -74,7 +74,7 @@ def oracle_problem(dev):
     if dev.seq_lens is not None:
         seq = dev.seq_lens.cpu().numpy()
     return O.Problem(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim, c.seq_len,
-                     q_bf16=c.q_dtype == "bf16", kv_bf16=c.kv_dtype == "bf16", scale=inp.scale,
+                     q_dtype=c.q_dtype, kv_dtype=c.kv_dtype, scale=inp.scale,
                      tile_len=dev.problem.s.tile_len, seq_lens=seq, page_size=c.page_size,
                      page_table=inp.page_table if c.page_size else None)
 

@@ -87,6 +87,8 @@ def test_workspace_sizes_follow_layout(lib):
     (dict(tile_len=192), UNSUPPORTED),                   # multiple of 64, not built
     (dict(head_dim=64), UNSUPPORTED),
     (dict(q_dtype=0), UNSUPPORTED),                      # q and KV dtypes differ
+    (dict(q_dtype=0, kv_dtype=2), UNSUPPORTED),          # e4m3 KV needs bf16 q
+    (dict(q_dtype=2, kv_dtype=2), INVALID),              # e4m3 is a KV storage only
     (dict(kv_dtype=7), INVALID),
     (dict(num_q_heads=24), UNSUPPORTED),                 # group of 3
     (dict(scale=0.0), INVALID),
@@ -111,6 +113,13 @@ def test_sample_count_validation(lib):
     assert _flash(lib, p, S=100) == INVALID              # 100 % 128 tiles != 0
     assert _flash(lib, p, S=128 * 300) == UNSUPPORTED    # 300 samples per 256-token tile
     assert _flash(lib, _problem(seq_lens=0x2000)) == INVALID   # ragged flash
+
+
+def test_fp8_kv_accepted(lib):
+    p = _problem(kv_dtype=2)                             # bf16 q, e4m3 K/V
+    st, n = _wsize(lib, p, PROP, 128)
+    assert st == OK and n == _wsize(lib, _problem(), PROP, 128)[1]
+    assert _prop(lib, p, ws_bytes=10) == WORKSPACE        # reaches the workspace check
 
 
 def test_sampler_validation(lib):

@@ -234,8 +234,38 @@ def test_exact_small(gpu, cid, kw):
     _say("exact", cid, rep)
 
 
+# ------------------------------------------------- e4m3 KV
+@pytest.mark.parametrize("T", [64, 256, 1024])
+def test_fp8_prop_small(gpu, T):
+    """e4m3 K and V with bf16 queries: prop against the oracle, which widens
+    the same bytes with its own decoder."""
+    import parity
+    cfg = synth.small_config(6, batch=2, seq_len=3000)
+    rep = parity.check_prop(_dev(cfg, 15, gpu, tile_len=T), 128)
+    _say("fp8 prop T", T, rep)
+
+
+def test_fp8_prop_samplers_flash_exact(gpu):
+    import parity
+    cfg = synth.small_config(6, batch=2, seq_len=3000)
+    dev = _dev(cfg, 16, gpu)
+    for smp in ("strat", "iid"):
+        _say("fp8", smp, parity.check_prop(dev, 96, sampler=smp))
+    _say("fp8 exact", parity.check_exact(dev))
+    cfg = synth.small_config(7, batch=2, seq_len=4096)
+    _say("fp8 flash", parity.check_flash(_dev(cfg, 17, gpu), 512))
+
+
+def test_fp8_paged_ragged(gpu):
+    import parity
+    cfg = synth.small_config(5, kv_dtype="fp8", batch=5, seq_len=4000, min_seq_len=300)
+    dev = _dev(cfg, 18, gpu)
+    _say("fp8 paged prop", parity.check_prop(dev, 128))
+    _say("fp8 paged exact", parity.check_exact(dev))
+
+
 # ------------------------------------------------- full-size workloads
-@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+@pytest.mark.parametrize("cid", [2, 3, 4, 5, 6, 7])
 def test_full_size_prop(gpu, cid):
     import parity
     cfg = synth.CONFIGS[cid]

@@ -413,7 +413,7 @@ def test_paged_equals_contiguous():
             pg = inp.page_table[b, j // P]
             kc[b, :, j] = inp.k[pg, :, j % P]
             vc[b, :, j] = inp.v[pg, :, j % P]
-    pc = O.Problem(B, cfg.num_q_heads, Hkv, d, n_max, q_bf16=True, kv_bf16=True,
+    pc = O.Problem(B, cfg.num_q_heads, Hkv, d, n_max, q_dtype="bf16", kv_dtype="bf16",
                    scale=inp.scale, tile_len=cfg.tile_len, seq_lens=inp.seq_lens)
     S = cfg.S
     a = O.santa_prop(prob, inp.q, inp.k, inp.v, S, inp.u(S))
@@ -433,7 +433,7 @@ def test_flash_golden():
     k = np.log(w).astype(np.float32).reshape(1, 1, n, 1)
     rng = np.random.default_rng(0)
     v = rng.standard_normal((1, 1, n, 1)).astype(np.float32)
-    prob = O.Problem(1, 1, 1, 1, n, q_bf16=False, kv_bf16=False, scale=1.0, tile_len=T)
+    prob = O.Problem(1, 1, 1, 1, n, q_dtype="f32", kv_dtype="f32", scale=1.0, tile_len=T)
     for pt in g["points"]:
         r = O.santa_flash(prob, q, k, v, S, np.array([pt["U"]], np.float32))
         assert r["idx"][0].tolist() == pt["idx"]
@@ -478,7 +478,7 @@ def test_flash_uniform_tiles_full_budget_is_exact():
     kd[..., 0] = k[..., 0]
     qd = np.zeros((1, 1, d), np.float32)
     qd[..., 0] = 1.0
-    prob = O.Problem(1, 1, 1, d, n, q_bf16=False, kv_bf16=False, scale=1.0, tile_len=T)
+    prob = O.Problem(1, 1, 1, d, n, q_dtype="f32", kv_dtype="f32", scale=1.0, tile_len=T)
     S = T * nt
     f = O.santa_flash(prob, qd, kd, v, S, np.array([0.3 / S], np.float32))
     ex = O.exact(prob, qd, kd, v)
@@ -517,7 +517,7 @@ def test_empty_request_reading():
     seq = inp.seq_lens.copy()
     seq[1] = 0
     prob = O.Problem(cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.seq_len,
-                     q_bf16=True, kv_bf16=True, scale=inp.scale, tile_len=cfg.tile_len,
+                     q_dtype="bf16", kv_dtype="bf16", scale=inp.scale, tile_len=cfg.tile_len,
                      seq_lens=seq, page_size=cfg.page_size, page_table=inp.page_table)
     S = cfg.S
     r = O.santa_prop(prob, inp.q, inp.k, inp.v, S, inp.u(S))
@@ -541,3 +541,43 @@ def test_bf16_rounding_matches_torch():
     np.testing.assert_array_equal(ours, ref)
     nan = synth.f32_to_bf16_bits(np.array([np.nan], np.float32))
     assert np.isnan(synth.bf16_bits_to_f32(nan))[0]
+
+
+def test_e4m3_storage_matches_torch():
+    """Synthetic e4m3 storage against torch's float8_e4m3fn: every code
+    decodes to the same value, and rounding is to nearest with ties to the
+    even code (midpoints between neighbouring codes included)."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    ours = synth.e4m3_bits_to_f32(codes)
+    np.testing.assert_array_equal(np.isnan(ours), np.isnan(ref))
+    np.testing.assert_array_equal(ours[~np.isnan(ref)], ref[~np.isnan(ref)])
+    rng = np.random.default_rng(1)
+    fin = ref[np.isfinite(ref)]
+    mags = np.unique(np.abs(fin))
+    mids = ((mags[1:] + mags[:-1]) / 2).astype(np.float32)          # exact ties
+    x = np.concatenate([rng.standard_normal(200000).astype(np.float32) * 4,
+                        rng.uniform(-448, 448, 20000).astype(np.float32),
+                        mids, -mids, np.array([0.0, -0.0, 2 ** -9, 2 ** -10, 448.0], np.float32)])
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = synth.f32_to_e4m3_bits(x)
+    np.testing.assert_array_equal(got, want)
+    assert synth.f32_to_e4m3_bits(np.array([1e6], np.float32))[0] == 0x7E     # saturates to 448
+
+
+def test_oracle_e4m3_widening_through_logits():
+    """The oracle widens e4m3 K by its own decoder: with q = e_0 (bf16 1.0)
+    and scale 1, the logit of row j is the value of the code stored in it,
+    for all 254 finite codes, and NaN for the two NaN codes."""
+    codes = np.arange(256, dtype=np.uint8)
+    d = 128
+    k = np.zeros((1, 1, 256, d), np.uint8)
+    k[0, 0, :, 0] = codes
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = 1.0
+    qb = synth.f32_to_bf16_bits(q)
+    prob = O.Problem(1, 1, 1, d, 256, q_dtype="bf16", kv_dtype="fp8", scale=1.0, tile_len=64)
+    x = O.logits(prob, qb, k, 0, 0)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    np.testing.assert_array_equal(np.isnan(x), np.isnan(ref))
+    np.testing.assert_array_equal(x[~np.isnan(ref)], ref[~np.isnan(ref)])
