@@ -79,7 +79,8 @@ __global__ __launch_bounds__(kBlock) void exact_partial_kernel(
     // instruction; the loads of VCH blocks are in flight together and rows
     // past the end read the block's row 0 with weight 0 (Pw is 0 there)
     constexpr int NSV = T / 64;
-    constexpr int VCH = NSV < 2 ? NSV : 2;
+    constexpr int VCH_MAX = sizeof(KV) == 1 ? 4 : 2;     // e4m3 rows: twice the blocks in flight
+    constexpr int VCH = NSV < VCH_MAX ? NSV : VCH_MAX;
     const int slot = lane >> 4, chunk = lane & 15;
     float acc[G][8];
 #pragma unroll

@@ -66,7 +66,10 @@ struct ScorerMfma {
     typedef float acc_t;
     static constexpr int NS = T / 64;
     static constexpr int NV = 4;
-    static constexpr int CH = NS < 2 ? NS : 2;   // steps whose K loads are in flight together
+    // steps whose K loads are in flight together: e4m3 rows are half as long,
+    // so twice as many steps keep the same bytes in flight
+    static constexpr int CH_MAX = sizeof(KV) == 1 ? 4 : 2;
+    static constexpr int CH = NS < CH_MAX ? NS : CH_MAX;
     static constexpr int kStageVec = kWavesPerBlock * 256;   // LDS staging, 16-byte units (4 KiB per wave)
     bf16x8_t qa[4];
     acc_t x[NS][NV];
