@@ -106,14 +106,25 @@ struct ScorerMfma {
 
     __device__ __forceinline__ void score(const KV *__restrict__ k, const KVLayout &L, int b, int g,
                                           int t0, int n, u32x4 *stage) {
-        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        const int lane = threadIdx.x & 63;
+        // paged: the wave index in a scalar register, so that the page
+        // lookups are scalar loads, and every block's lookup issued first, so
+        // that they overlap instead of preceding each chunk's K loads
+        const int w = PAGED ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : (int)(threadIdx.x >> 6);
         const int tok = lane & 15, kq = lane >> 4;
         u32x4 *wst = stage + w * 256;
+        size_t base_all[PAGED ? NS : 1];
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) base_all[s] = block_base<PAGED>(L, b, g, t0 + 64 * s + 16 * w, n, t0);
+        }
 #pragma unroll
         for (int s0 = 0; s0 < NS; s0 += CH) {
             size_t base[CH];
 #pragma unroll
-            for (int ii = 0; ii < CH; ++ii) base[ii] = block_base<PAGED>(L, b, g, t0 + 64 * (s0 + ii) + 16 * w, n, t0);
+            for (int ii = 0; ii < CH; ++ii)
+                base[ii] = PAGED ? base_all[PAGED ? s0 + ii : 0]
+                                 : block_base<PAGED>(L, b, g, t0 + 64 * (s0 + ii) + 16 * w, n, t0);
             u32x4 kv[CH][kLoads];
 #pragma unroll
             for (int ii = 0; ii < CH; ++ii) {
