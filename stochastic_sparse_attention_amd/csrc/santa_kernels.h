@@ -11,8 +11,11 @@
 
 namespace santa {
 
-constexpr int kSampleBlock = 1024;                 // threads of the per-head sampling block
-constexpr int kSampleWaves = kSampleBlock / kWave;
+#ifndef SANTA_SAMPLE_MANY_HEADS
+#define SANTA_SAMPLE_MANY_HEADS 512
+#endif
+// above this many heads the systematic sampling kernel runs 8 waves per head
+constexpr int kSampleManyHeads = SANTA_SAMPLE_MANY_HEADS;
 constexpr int kMergeBlock = 1024;                  // threads of the per-head merge block
 constexpr int kMergeParts = kMergeBlock / kHeadDim;
 

@@ -63,6 +63,6 @@ hipError_t launch_prop(const LaunchArgs &a, const TimingHook &hook);
 hipError_t launch_flash(const LaunchArgs &a, const TimingHook &hook);
 hipError_t launch_exact(const LaunchArgs &a, const TimingHook &hook);
 size_t visit_record_bytes();
-size_t prop_sample_lds_bytes(int kcap, int S, int sampler);
+size_t prop_sample_lds_bytes(int kcap, int S, int sampler, int max_nt);
 
 }  // namespace santa

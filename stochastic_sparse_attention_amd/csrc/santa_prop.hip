@@ -132,7 +132,7 @@ struct VisitRec {
     float a, b;
 };
 
-constexpr int kMaxTilesLds = 1024;   // tiles per request the reducer keeps in LDS
+constexpr int kRegisterTiles = 256;  // up to this many tiles the reducer keeps them in registers
 constexpr int kGatherRounds = 4;     // V rows per lane slot in flight together in the gather
 
 // EPL consecutive floats from a 16-byte aligned address (EPL = T/64)
@@ -380,7 +380,7 @@ __device__ __forceinline__ void reduce_head(const float2 *__restrict__ stp, int 
         reduce_in_registers<1>(stp, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out);
     else if (nt <= 128)
         reduce_in_registers<2>(stp, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out);
-    else if (nt <= 256)
+    else if (nt <= kRegisterTiles)
         reduce_in_registers<4>(stp, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out);
     else
         reduce_with_lds(stp, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out, R);
@@ -401,12 +401,14 @@ __device__ __forceinline__ int count_below(const double *thr, int len, double F)
 // workgroups share a compute unit
 // LIST: stratified / i.i.d. thresholds (a sorted list in LDS); else the
 // systematic closed form
-template <typename KV, int T, bool PAGED, bool LIST>
-__global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8))) void prop_sample_kernel(
+// NW: waves per workgroup (16, or 8 for many heads: more heads per CU)
+template <typename KV, int T, bool PAGED, bool LIST, int NW>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(8))) void prop_sample_kernel(
     const KV *__restrict__ v, KVLayout L, const int *__restrict__ seq_lens, int batch, int num_q_heads,
     int G, int S, int max_nt, int kcap, int sampler, const float *__restrict__ u, float scale,
     const float *__restrict__ stash, const float2 *__restrict__ stats, float *__restrict__ out,
     int *__restrict__ sample_idx, int *__restrict__ tile_budget) {
+    constexpr int SB = NW * kWave;                  // threads per workgroup
     extern __shared__ __align__(16) unsigned char smem[];
     // stratified / i.i.d.: the sorted thresholds first (padded to a power of
     // two for the sort), then the visit list and the marker arrays
@@ -416,14 +418,19 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
     VisitRec *vis = reinterpret_cast<VisitRec *>(smem + (size_t)np * sizeof(double));   // [kcap]
     int *jsel = reinterpret_cast<int *>(smem + (size_t)np * sizeof(double) + (size_t)kcap * sizeof(VisitRec));   // [S] marker rows, -1 elsewhere
     int *jmul = jsel + S;                                                  // [S] marker multiplicities
-    __shared__ float red[kSampleWaves][kHeadDim];
-    __shared__ float2 tstat[kMaxTilesLds];          // reducer: per-tile (m_t, Z_t)
-    __shared__ double tf[kMaxTilesLds];             // reducer: e^{scale (m_t - M)}
-    __shared__ double tC[kMaxTilesLds];             // reducer: tile CDF C_t
-    __shared__ int tcn[kMaxTilesLds];               // reducer: thresholds below C_t
+    // per-tile arrays of the LDS reducer (more than 256 tiles; sized only
+    // when max_nt needs them): (m_t, Z_t), e^{scale (m_t - M)}, C_t, counts
+    unsigned char *rbase = reinterpret_cast<unsigned char *>(jmul + S);
+    rbase += (8 - ((uintptr_t)rbase & 7)) & 7;
+    const int rn = max_nt > kRegisterTiles ? max_nt : 0;
+    double *tf = reinterpret_cast<double *>(rbase);
+    double *tC = tf + rn;
+    float2 *tstat = reinterpret_cast<float2 *>(tC + rn);
+    int *tcn = reinterpret_cast<int *>(tstat + rn);
+    __shared__ float red[NW][kHeadDim];
     __shared__ int nvis_sh;
-    __shared__ int wrow[kSampleWaves][kWave];        // per-wave compacted marker rows
-    __shared__ float wmul[kSampleWaves][kWave];      // and their multiplicities
+    __shared__ int wrow[NW][kWave];        // per-wave compacted marker rows
+    __shared__ float wmul[NW][kWave];      // and their multiplicities
 
     // block -> (request, KV head, head in group); blocks of one KV head are
     // numbered bg + i * B*Hkv, the numbering pass 1 uses for that head's tiles
@@ -437,9 +444,9 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
 
     if (nt == 0) {                                  // empty request
         if (tile_budget)
-            for (int t = tid; t < max_nt; t += kSampleBlock) tile_budget[(size_t)bh * max_nt + t] = 0;
+            for (int t = tid; t < max_nt; t += SB) tile_budget[(size_t)bh * max_nt + t] = 0;
         if (sample_idx)
-            for (int m = tid; m < S; m += kSampleBlock) sample_idx[(size_t)bh * S + m] = -1;
+            for (int m = tid; m < S; m += SB) sample_idx[(size_t)bh * S + m] = -1;
         if (tid < kHeadDim) out[(size_t)bh * kHeadDim + tid] = 0.f;
         return;
     }
@@ -449,7 +456,7 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
     if constexpr (LIST) {
         const float *ub = u + (size_t)bh * S;
         const double kBelowOne = 1.0 - 0x1p-53;
-        for (int m = tid; m < np; m += kSampleBlock) {
+        for (int m = tid; m < np; m += SB) {
             double x = INFINITY;                        // sort padding
             if (m < S) {
                 x = (double)ub[m];
@@ -464,7 +471,7 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
             // bitonic sort of the np slots, ascending
             for (int k2 = 2; k2 <= np; k2 <<= 1) {
                 for (int j2 = k2 >> 1; j2 > 0; j2 >>= 1) {
-                    for (int i = tid; i < np; i += kSampleBlock) {
+                    for (int i = tid; i < np; i += SB) {
                         const int p = i ^ j2;
                         if (p > i) {
                             const double a = thr[i], c = thr[p];
@@ -484,7 +491,7 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
     // ---------------- reducer: wave 0, lane l owns tiles [l*CH, l*CH + CH);
     // the other waves clear the marker positions meanwhile
     if (w != 0) {
-        for (int m = tid - kWave; m < S; m += kSampleBlock - kWave) jsel[m] = -1;
+        for (int m = tid - kWave; m < S; m += SB - kWave) jsel[m] = -1;
     } else {
         const float2 *stp = stats + (size_t)bh * max_nt;
         int *budget = tile_budget ? tile_budget + (size_t)bh * max_nt : nullptr;
@@ -507,7 +514,7 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int k0 = w * TPW; k0 < nvis; k0 += TPW * kSampleWaves) {
+    for (int k0 = w * TPW; k0 < nvis; k0 += TPW * NW) {
         const int kv = k0 + sub;
         const bool active = kv < nvis;
         const VisitRec rec = vis[active ? kv : k0];
@@ -650,7 +657,7 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
     if (tid < kHeadDim) {
         float sum = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < kSampleWaves; ++ww) sum += red[ww][tid];
+        for (int ww = 0; ww < NW; ++ww) sum += red[ww][tid];
         // divide by S: for a power of two this is an exact exponent shift
         const bool pow2 = (S & (S - 1)) == 0;
         out[(size_t)bh * kHeadDim + tid] = pow2 ? sum * (1.0f / (float)S) : sum / (float)S;
@@ -660,9 +667,10 @@ __global__ __launch_bounds__(kSampleBlock) __attribute__((amdgpu_waves_per_eu(8)
 // ===================================================================
 // launchers
 // ===================================================================
-size_t prop_sample_lds_bytes(int kcap, int S, int sampler) {
+size_t prop_sample_lds_bytes(int kcap, int S, int sampler, int max_nt) {
     const size_t thr = sampler == kSamplerSys ? 0 : (size_t)threshold_slots(S, sampler) * sizeof(double);
-    return thr + (size_t)kcap * sizeof(VisitRec) + 2 * (size_t)S * sizeof(int);
+    const size_t red = max_nt > kRegisterTiles ? 8 + (size_t)max_nt * (2 * sizeof(double) + sizeof(float2) + sizeof(int)) : 0;
+    return thr + (size_t)kcap * sizeof(VisitRec) + 2 * (size_t)S * sizeof(int) + red;
 }
 
 template <typename KV, int G, int T, bool PAGED>
@@ -685,24 +693,25 @@ static hipError_t launch_prop_t(const LaunchArgs &a, const TimingHook &hook) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int BH = a.batch * a.num_q_heads;
-    const size_t lds = prop_sample_lds_bytes(a.kmax, a.S, a.sampler);
-    if (a.sampler == kSamplerSys) {
-        hipLaunchKernelGGL((prop_sample_kernel<KV, T, PAGED, false>), dim3((unsigned)BH), dim3(kSampleBlock), lds,
-                           st, (const KV *)a.v, L, a.seq_lens, a.batch, a.num_q_heads, G, a.S, max_nt, a.kmax,
-                           a.sampler, a.u, a.scale, (const float *)stash, (const float2 *)stats, a.out,
-                           a.sample_idx, a.tile_budget);
+    const size_t lds = prop_sample_lds_bytes(a.kmax, a.S, a.sampler, max_nt);
+    // few heads: 16 waves per head; many heads (systematic thresholds): 8,
+    // so that more heads (and their dependent memory round trips) share
+    // each compute unit
+    const bool many = BH > kSampleManyHeads && a.sampler == kSamplerSys;
+    auto launch = [&](auto kernel, int nw) -> hipError_t {
+        if (lds > 64 * 1024) {
+            const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (ea != hipSuccess) return ea;
+        }
+        hipLaunchKernelGGL(kernel, dim3((unsigned)BH), dim3(nw * kWave), lds, st, (const KV *)a.v, L, a.seq_lens,
+                           a.batch, a.num_q_heads, G, a.S, max_nt, a.kmax, a.sampler, a.u, a.scale,
+                           (const float *)stash, (const float2 *)stats, a.out, a.sample_idx, a.tile_budget);
         return hipGetLastError();
-    }
-    if (lds > 64 * 1024) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prop_sample_kernel<KV, T, PAGED, true>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((prop_sample_kernel<KV, T, PAGED, true>), dim3((unsigned)BH), dim3(kSampleBlock), lds, st,
-                       (const KV *)a.v, L, a.seq_lens, a.batch, a.num_q_heads, G, a.S, max_nt, a.kmax,
-                       a.sampler, a.u, a.scale, (const float *)stash, (const float2 *)stats, a.out,
-                       a.sample_idx, a.tile_budget);
-    return hipGetLastError();
+    };
+    if (a.sampler != kSamplerSys) return launch(prop_sample_kernel<KV, T, PAGED, true, 16>, 16);
+    if (many) return launch(prop_sample_kernel<KV, T, PAGED, false, 8>, 8);
+    return launch(prop_sample_kernel<KV, T, PAGED, false, 16>, 16);
 }
 
 hipError_t launch_prop(const LaunchArgs &a, const TimingHook &hook) { SANTA_DISPATCH(launch_prop_t) }

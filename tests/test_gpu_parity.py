@@ -121,6 +121,16 @@ def test_sampler_variance_ordering(gpu):
     assert mse["sys"] < mse["iid"] and mse["strat"] < mse["iid"]
 
 
+def test_prop_many_heads(gpu):
+    """More than 512 heads: the systematic sampling kernel runs 8 waves per
+    head.  Mixed lengths (some short requests), paged KV and S = 1000."""
+    import parity
+    cfg = synth.small_config(5, batch=24, seq_len=2500, min_seq_len=64)
+    dev = _dev(cfg, 19, gpu)
+    _say("768 heads, S=128", parity.check_prop(dev, 128))
+    _say("768 heads, S=1000", parity.check_prop(dev, 1000, repeat=False))
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (32, 8), (16, 2)])
 def test_prop_gqa_groups(gpu, hq, hkv):
     import parity
