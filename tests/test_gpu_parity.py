@@ -223,6 +223,23 @@ def test_flash_small(gpu, T, S):
     _say("flash", T, S, rep)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_flash_paged_uniform(gpu, kv):
+    """Flash over a paged cache: every request has max_seq_len keys, so the
+    problem carries a page table but no per-request lengths."""
+    import dataclasses
+    import parity
+    from stochastic_sparse_attention_amd import Problem
+    cfg = synth.small_config(5, batch=3, seq_len=4096, min_seq_len=4096, kv_dtype=kv)
+    dev = _dev(cfg, 20, gpu)
+    prob = Problem(cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.seq_len,
+                   dtype=cfg.q_dtype, kv_dtype=cfg.kv_dtype, scale=float(dev.inp.scale),
+                   tile_len=cfg.tile_len, page_size=cfg.page_size, page_table=dev.page_table)
+    dev = dataclasses.replace(dev, problem=prob, seq_lens=None)
+    _say("flash paged", kv, parity.check_flash(dev, 512))
+    _say("prop paged uniform", kv, parity.check_prop(dev, 128, repeat=False))
+
+
 def test_flash_ragged_last_tile(gpu):
     import parity
     cfg = synth.small_config(3, batch=1, seq_len=1000)      # 4 tiles, last has 232 rows
