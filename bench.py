@@ -78,6 +78,10 @@ def time_steps(fn, steps, warmup, events=None):
     t1 = time.perf_counter()
     kern = None
     if events:
+        # default HIP events, recorded by the dispatch itself: their
+        # system-scope fences slow the bracketed kernel, but they time that
+        # kernel exactly (events created with hipEventDisableSystemFence
+        # leave it alone but then include its dispatch latency)
         pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for _ in range(steps)]
         for a, b in pairs:          # create the HIP events (torch creates them on first record)

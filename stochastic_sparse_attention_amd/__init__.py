@@ -108,9 +108,14 @@ def exact_decode_ref(problem: Problem, q, k, v, out, workspace=None, stream=None
     return ws
 
 
+def _event_handle(ev):
+    if ev is None:
+        return None
+    return C.c_void_p(ev.cuda_event if hasattr(ev, "cuda_event") else int(ev))
+
+
 def santa_set_timing_events(begin=None, end=None):
-    """Record `begin`/`end` (torch.cuda.Event) around the dominant kernel of
-    later calls on this thread; None, None turns it off."""
-    b = None if begin is None else C.c_void_p(begin.cuda_event)
-    e = None if end is None else C.c_void_p(end.cuda_event)
-    _lib.load().santa_set_timing_events(b, e)
+    """Record `begin`/`end` (torch.cuda.Event, or raw hipEvent_t handles)
+    around the dominant kernel of later calls on this thread; None, None turns
+    it off."""
+    _lib.load().santa_set_timing_events(_event_handle(begin), _event_handle(end))
