@@ -304,3 +304,53 @@ def test_full_size_prop(gpu, cid):
         _say("full exact cfg", cid, parity.check_exact(dev, repeat=False))
     if "flash" in cfg.variants:
         _say("full flash cfg", cid, parity.check_flash(dev, cfg.S_flash, repeat=False))
+
+
+# ------------------------------------------------- HIP graph replay
+def test_graph_replays_match_eager(gpu):
+    """prop (all three threshold generators) and exact decode captured in one
+    HIP graph: every replay, with eager work and synchronisations in
+    between, gives results bitwise equal to the eager calls."""
+    import torch
+    import stochastic_sparse_attention_amd as sa
+    cfg = synth.small_config(2, batch=2, seq_len=3000)
+    dev = _dev(cfg, 21, gpu)
+    S, BH = 128, cfg.batch * cfg.num_q_heads
+    max_nt = (cfg.seq_len + cfg.tile_len - 1) // cfg.tile_len
+    U, uu = dev.u(S), dev.uniforms(S)
+    ws = torch.empty(sa.santa_workspace_size(dev.problem, "prop", S), dtype=torch.uint8, device=gpu)
+    wse = torch.empty(sa.santa_workspace_size(dev.problem, "exact"), dtype=torch.uint8, device=gpu)
+    outs = {k: torch.empty((BH, 128), dtype=torch.float32, device=gpu) for k in ("sys", "strat", "iid", "exact")}
+    idx = torch.empty((BH, S), dtype=torch.int32, device=gpu)
+    tb = torch.empty((BH, max_nt), dtype=torch.int32, device=gpu)
+
+    def step():
+        sa.santa_decode_prop(dev.problem, dev.q, dev.k, dev.v, S, U, outs["sys"], idx, tb, workspace=ws)
+        for smp in ("strat", "iid"):
+            sa.santa_decode_prop_sampler(dev.problem, dev.q, dev.k, dev.v, S, smp, uu, outs[smp], workspace=ws)
+        sa.exact_decode_ref(dev.problem, dev.q, dev.k, dev.v, outs["exact"], workspace=wse)
+
+    step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in outs.items()}
+    ref_idx, ref_tb = idx.clone(), tb.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    scratch = torch.randn(1 << 20, device=gpu)
+    for rep in range(3):
+        for v in outs.values():
+            v.fill_(float("nan"))
+        idx.fill_(-5)
+        tb.fill_(-5)
+        scratch.mul_(1.0001)                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(outs[k].view(torch.int32), ref[k].view(torch.int32)), (rep, k)
+        assert torch.equal(idx, ref_idx) and torch.equal(tb, ref_tb), rep
+    _say("graph replays match eager")
