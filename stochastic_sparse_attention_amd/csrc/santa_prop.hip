@@ -514,6 +514,45 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(8)))
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    // gather of the markers at positions [m_lo, m_hi), 64 at a time: they
+    // are compacted into the wave's LDS list, then read 4 rows per wave
+    // instruction with every load of a round in flight together; each row
+    // is weighed by its multiplicity
+    auto gather_range = [&](int m_lo, int m_hi) {
+        for (int c = m_lo; c < m_hi; c += kWave) {
+            const int m = c + lane;
+            const int r = (m < m_hi) ? jsel[m] : -1;
+            const unsigned long long bal = __ballot(r >= 0);
+            const int nm = __popcll(bal);
+            if (r >= 0) {
+                const int pos = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+                wrow[w][pos] = r;
+                wmul[w][pos] = (float)jmul[m];
+            }
+            wave_sync_lds();
+            for (int i0 = 0; i0 < nm; i0 += 4 * kGatherRounds) {
+                int rows[kGatherRounds];
+                float mul[kGatherRounds];
+#pragma unroll
+                for (int u = 0; u < kGatherRounds; ++u) {
+                    // slots past the list re-read its first row with weight 0
+                    const int idx = i0 + slot + 4 * u;
+                    rows[u] = wrow[w][idx < nm ? idx : 0];
+                    mul[u] = idx < nm ? wmul[w][idx] : 0.f;
+                }
+                float xv[kGatherRounds][8];
+#pragma unroll
+                for (int u = 0; u < kGatherRounds; ++u) load_v8<KV>(v + row_offset(L, b, g, rows[u]) + 8 * chunk, xv[u]);
+#pragma unroll
+                for (int u = 0; u < kGatherRounds; ++u)
+#pragma unroll
+                    for (int e2 = 0; e2 < 8; ++e2) acc[e2] = fmaf(mul[u], xv[u][e2], acc[e2]);
+            }
+            wave_sync_lds();
+        }
+    };
+    const bool multi = nvis > TPW * NW;        // some wave takes more than one round of tiles
     for (int k0 = w * TPW; k0 < nvis; k0 += TPW * NW) {
         const int kv = k0 + sub;
         const bool active = kv < nvis;
@@ -608,41 +647,14 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(8)))
                 carry = __builtin_amdgcn_readlane(pm, 63);
             }
         }
-        // gather: the markers of [m0, m1), 64 positions at a time, are
-        // compacted into the wave's LDS list, then read 4 rows per wave
-        // instruction with every load of a round in flight together
-        for (int c = m0; c < m1; c += kWave) {
-            const int m = c + lane;
-            const int r = (m < m1) ? jsel[m] : -1;
-            const unsigned long long bal = __ballot(r >= 0);
-            const int nm = __popcll(bal);
-            if (r >= 0) {
-                const int pos = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
-                wrow[w][pos] = r;
-                wmul[w][pos] = (float)jmul[m];
-            }
-            wave_sync_lds();
-            for (int i0 = 0; i0 < nm; i0 += 4 * kGatherRounds) {
-                int rows[kGatherRounds];
-                float mul[kGatherRounds];
-#pragma unroll
-                for (int u = 0; u < kGatherRounds; ++u) {
-                    // slots past the list re-read its first row with weight 0
-                    const int idx = i0 + slot + 4 * u;
-                    rows[u] = wrow[w][idx < nm ? idx : 0];
-                    mul[u] = idx < nm ? wmul[w][idx] : 0.f;
-                }
-                float xv[kGatherRounds][8];
-#pragma unroll
-                for (int u = 0; u < kGatherRounds; ++u) load_v8<KV>(v + row_offset(L, b, g, rows[u]) + 8 * chunk, xv[u]);
-#pragma unroll
-                for (int u = 0; u < kGatherRounds; ++u)
-#pragma unroll
-                    for (int e2 = 0; e2 < 8; ++e2) acc[e2] = fmaf(mul[u], xv[u][e2], acc[e2]);
-            }
-            wave_sync_lds();
-        }
+        if (!multi) gather_range(m0, m1);
+    }
+    if (multi) {
+        // more than one round of tiles per wave: the gather waits for every
+        // marker and then reads all of them in one round, 64 positions per
+        // wave at a time, instead of one V round trip per round of tiles
+        __syncthreads();
+        for (int c = w * kWave; c < S; c += NW * kWave) gather_range(c, min(c + kWave, S));
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
