@@ -71,6 +71,7 @@ def lib():
         L.oracle_santa_prop.argtypes = [P, vp, vp, vp, C.c_int, fp, dp, ip, dp, ip]
         L.oracle_santa_prop_sampler.argtypes = [P, vp, vp, vp, C.c_int, C.c_int, fp, dp, ip, dp, ip]
         L.oracle_santa_flash.argtypes = [P, vp, vp, vp, C.c_int, fp, dp, ip, dp, dp]
+        L.oracle_santa_flash_sampler.argtypes = [P, vp, vp, vp, C.c_int, C.c_int, fp, dp, ip, dp, dp]
         L.oracle_exact.argtypes = [P, vp, vp, vp, dp]
         L.oracle_replay.argtypes = [P, vp, C.c_int, ip, dp, C.c_int, dp]
         L.oracle_estimate_from_weights.argtypes = [dp, C.c_int, dp, C.c_int, dp, C.c_int, dp]
@@ -269,6 +270,24 @@ def santa_flash(prob: Problem, q, k, v, S, u):
                                   _dptr(out), _iptr(idx), _dptr(dl), _dptr(pt))
     if rc:
         raise ValueError(f"oracle_santa_flash: {rc}")
+    return {"out": out, "idx": idx, "delta": dl, "ptile": pt}
+
+
+def santa_flash_sampler(prob: Problem, q, k, v, S, sampler, u):
+    """S2ANTA-flash with the "sys", "strat" or "iid" generator per tile.
+    u: [B*Hq] offsets for sys; [B*Hq, S] uniforms (tile-major) otherwise."""
+    BH, d = prob.batch * prob.num_q_heads, prob.head_dim
+    nt = prob.max_tiles()
+    u = np.ascontiguousarray(u, np.float32)
+    out = np.empty((BH, d), np.float64)
+    idx = np.empty((BH, S), np.int32)
+    dl = np.empty((BH, S), np.float64)
+    pt = np.empty((BH, nt), np.float64)
+    rc = lib().oracle_santa_flash_sampler(prob.ref, _vp(q), _vp(k), _vp(v), S, SAMPLERS[sampler],
+                                          u.ctypes.data_as(C.POINTER(C.c_float)),
+                                          _dptr(out), _iptr(idx), _dptr(dl), _dptr(pt))
+    if rc:
+        raise ValueError(f"oracle_santa_flash_sampler: {rc}")
     return {"out": out, "idx": idx, "delta": dl, "ptile": pt}
 
 

@@ -363,11 +363,19 @@ int oracle_santa_prop(const oracle_problem *p, const void *q, const void *k,
 /*   ptile [B*Hq*n_t] p_t (NULL allowed), for replay                    */
 /* Requires uniform sequence length and S % n_t == 0.                   */
 /* ------------------------------------------------------------------ */
-int oracle_santa_flash(const oracle_problem *p, const void *q, const void *k,
-                       const void *v, int S, const float *u, double *out,
-                       int *idx, double *delta, double *ptile)
+/* The generators of key design 1, applied to each tile's own softmax with
+   its S_f = S/n_t samples:
+     kind 0  systematic: u [B*Hq], one offset U per head in [0, 1/S);
+             local thresholds u_f + m/S_f, u_f = U n_t (R6)
+     kind 1  stratified: u [B*Hq*S] in [0,1), tile-major (tile t's uniforms
+             at t*S_f .. t*S_f + S_f - 1); local thresholds (m + u_m)/S_f
+     kind 2  i.i.d.: u as for kind 1; local thresholds = the tile's
+             uniforms, sorted */
+int oracle_santa_flash_sampler(const oracle_problem *p, const void *q, const void *k,
+                               const void *v, int S, int kind, const float *u, double *out,
+                               int *idx, double *delta, double *ptile)
 {
-    if (p->seq_lens || !lengths_ok(p)) return -1;
+    if (p->seq_lens || !lengths_ok(p) || kind < 0 || kind > 2) return -1;
     int n = p->max_seq_len, nt = num_tiles(p, n);
     if (S <= 0 || S % nt) return -1;
     int Sf = S / nt, H = p->num_q_heads, d = p->head_dim, T = p->tile_len;
@@ -382,19 +390,38 @@ int oracle_santa_flash(const oracle_problem *p, const void *q, const void *k,
         double *zt = (double *)malloc(sizeof(double) * (size_t)nt);
         double *ot = (double *)malloc(sizeof(double) * (size_t)nt * d);
         double *t = (double *)malloc(sizeof(double) * (size_t)Sf);
+        double *u01 = (double *)malloc(sizeof(double) * (size_t)Sf);
         int *J = (int *)malloc(sizeof(int) * (size_t)Sf);
         double *dl = (double *)malloc(sizeof(double) * (size_t)Sf);
         oracle_logits(p, q, k, b, h, x);
-        double U = (double)u[bh];
-        if (!(U >= 0.0 && U < 1.0 / (double)S)) {
+        double uf = 0.0;
+        if (kind == 0) {
+            double U = (double)u[bh];
+            if (!(U >= 0.0 && U < 1.0 / (double)S)) {
 #pragma omp atomic write
-            status = -3;
+                status = -3;
+            }
+            uf = U * (double)nt;
         }
-        double uf = U * (double)nt;
         for (int tt = 0; tt < nt; ++tt) {
             int j0 = tt * T, len = (n - j0 < T) ? n - j0 : T;
             zt[tt] = oracle_softmax_weights(x + j0, len, e, &mt[tt]);
-            oracle_sys_thresholds(uf, Sf, t);
+            if (kind == 0) {
+                oracle_sys_thresholds(uf, Sf, t);
+            } else {
+                for (int m = 0; m < Sf; ++m) {
+                    u01[m] = (double)u[(size_t)bh * S + (size_t)tt * Sf + m];
+                    if (!(u01[m] >= 0.0 && u01[m] < 1.0)) {
+#pragma omp atomic write
+                        status = -3;
+                        u01[m] = 0.0;
+                    }
+                }
+                if (kind == 1)
+                    oracle_strat_thresholds(u01, Sf, t);
+                else
+                    oracle_iid_thresholds(u01, Sf, t);
+            }
             if (oracle_invert_cdf(e, len, t, Sf, J, dl) != 0) {
 #pragma omp atomic write
                 status = -4;
@@ -415,9 +442,17 @@ int oracle_santa_flash(const oracle_problem *p, const void *q, const void *k,
             if (ptile) ptile[(size_t)bh * nt + tt] = pt;
             for (int i = 0; i < d; ++i) o[i] += pt * ot[(size_t)tt * d + i];
         }
-        free(x); free(e); free(mt); free(zt); free(ot); free(t); free(J); free(dl);
+        free(x); free(e); free(mt); free(zt); free(ot); free(t); free(u01); free(J); free(dl);
     }
     return status;
+}
+
+/* S2ANTA-flash with systematic thresholds. */
+int oracle_santa_flash(const oracle_problem *p, const void *q, const void *k,
+                       const void *v, int S, const float *u, double *out,
+                       int *idx, double *delta, double *ptile)
+{
+    return oracle_santa_flash_sampler(p, q, k, v, S, 0, u, out, idx, delta, ptile);
 }
 
 /* ------------------------------------------------------------------ */

@@ -452,6 +452,38 @@ def test_flash_single_tile_is_systematic():
     np.testing.assert_allclose(f["out"], a["out"], rtol=0, atol=1e-15)
 
 
+@pytest.mark.parametrize("sampler", ["strat", "iid"])
+def test_flash_sampler_single_tile_is_prop(sampler):
+    """One tile holding every token: the tile's S_f = S local thresholds are
+    the global ones, so flash selects what prop selects."""
+    inp, prob = _small_inputs(1, tile_len=1024)
+    S = inp.cfg.S
+    u = np.random.default_rng(5).random((1, S)).astype(np.float32)
+    a = O.santa_prop_sampler(prob, inp.q, inp.k, inp.v, S, sampler, u)
+    f = O.santa_flash_sampler(prob, inp.q, inp.k, inp.v, S, sampler, u)
+    assert np.array_equal(a["idx"], f["idx"])
+    np.testing.assert_allclose(f["out"], a["out"], rtol=0, atol=1e-15)
+
+
+def test_flash_strat_uniform_tiles_full_budget_is_exact():
+    """Constant logits inside each tile and S_f = T stratified thresholds:
+    stratum m of a tile lies in token m's cell, every token is taken once
+    and the merged estimate is AV."""
+    T, nt, d = 8, 4, 3
+    n = T * nt
+    rng = np.random.default_rng(9)
+    kd = np.zeros((1, 1, n, d), np.float32)
+    kd[..., 0] = np.repeat(rng.standard_normal(nt), T).astype(np.float32).reshape(1, 1, n)
+    qd = np.zeros((1, 1, d), np.float32)
+    qd[..., 0] = 1.0
+    v = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+    prob = O.Problem(1, 1, 1, d, n, q_dtype="f32", kv_dtype="f32", scale=1.0, tile_len=T)
+    u = rng.random((1, n)).astype(np.float32)
+    f = O.santa_flash_sampler(prob, qd, kd, v, n, "strat", u)
+    assert np.array_equal(f["idx"][0], np.arange(n))
+    np.testing.assert_allclose(f["out"], O.exact(prob, qd, kd, v), rtol=0, atol=1e-13)
+
+
 def test_flash_expectation_equals_exact():
     for seed in (1, 3):
         inp, prob = _small_inputs(1, seed=seed)
