@@ -405,6 +405,15 @@ def main(argv=None):
             "tile_kernel_GB/s": round(fb["tile"] / (np.mean(fkern) * 1e-3) / 1e9, 1),
             "prop_speedup_vs_flash": round(fms / ms, 3),
         }
+        if not args.no_samplers:
+            uuf = dev.uniforms(Sf)
+            for smp in ("strat", "iid"):
+                def fsmp_step(i, smp=smp):
+                    c = i % ncopy
+                    sa.santa_decode_flash_sampler(dev.problem, dev.q, ks[c], vs[c], Sf, smp, uuf, outf, workspace=wsf)
+                fsms, _fk = time_steps(fsmp_step, args.steps, args.warmup)
+                log(f"bench: flash with {smp} thresholds {fsms * 1e3:.2f} us/step (eager)")
+                result["santa_flash"][f"{smp}_us_per_step"] = round(fsms * 1e3, 3)
 
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")

@@ -174,6 +174,25 @@ int santa_decode_flash(const santa_problem *p, const void *q, const void *k, con
                        void *stream);
 
 /*
+ * S2ANTA-flash with a choice of threshold generator ("key design 1" applied
+ * to each tile's own softmax; santa_decode_flash is this call with
+ * SANTA_SAMPLER_SYS).  Each tile takes S_f = S / n_t samples:
+ *   SANTA_SAMPLER_SYS    u [B*Hq] offsets in [0, 1/S); local thresholds
+ *                        u_f + m/S_f with u_f = U * n_t
+ *   SANTA_SAMPLER_STRAT  u [B*Hq, S] uniforms in [0, 1), tile-major (tile t's
+ *                        at t*S_f .. t*S_f + S_f - 1); local thresholds
+ *                        (m + u_m)/S_f
+ *   SANTA_SAMPLER_IID    u as for STRAT; local thresholds: the tile's
+ *                        uniforms, sorted on the device
+ * Uniforms outside [0, 1) are clamped into it (NaN counts as 0).  Other
+ * arguments, requirements and the workspace as for santa_decode_flash.
+ */
+int santa_decode_flash_sampler(const santa_problem *p, const void *q, const void *k, const void *v,
+                               int32_t S, int32_t sampler, const float *u, float *out,
+                               int32_t *sample_idx, int32_t *tile_budget, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
  * Exact split-KV decode on the same GPU: out = softmax(scale * q K^T) V per
  * head, computed per tile (max, sum, weighted V sum) and merged.  This is
  * the baseline that S2ANTA is measured against.

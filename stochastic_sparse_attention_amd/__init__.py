@@ -16,6 +16,7 @@ from ._lib import SantaError, santa_problem, SANTA_F32, SANTA_BF16, SANTA_FP8_E4
 
 __all__ = [
     "Problem", "santa_workspace_size", "santa_decode_prop", "santa_decode_prop_sampler", "santa_decode_flash",
+    "santa_decode_flash_sampler",
     "exact_decode_ref", "santa_set_timing_events", "SantaError",
 ]
 
@@ -97,6 +98,17 @@ def santa_decode_flash(problem: Problem, q, k, v, S, u, out, sample_idx=None, ti
                                         _ptr(sample_idx), _ptr(tile_budget), _ptr(ws), ws.numel(),
                                         _stream(stream))
     _lib._check("santa_decode_flash", st)
+    return ws
+
+
+def santa_decode_flash_sampler(problem: Problem, q, k, v, S, sampler, u, out, sample_idx=None,
+                               tile_budget=None, workspace=None, stream=None):
+    """sampler: "sys" (u: [B*Hq] offsets), "strat" or "iid" (u: [B*Hq, S] uniforms, tile-major)."""
+    ws = _workspace(problem, "flash", S, workspace, q.device)
+    st = _lib.load().santa_decode_flash_sampler(problem.ref, _ptr(q), _ptr(k), _ptr(v), S, SAMPLER[sampler],
+                                                _ptr(u), _ptr(out), _ptr(sample_idx), _ptr(tile_budget),
+                                                _ptr(ws), ws.numel(), _stream(stream))
+    _lib._check("santa_decode_flash_sampler", st)
     return ws
 
 

@@ -198,6 +198,14 @@ int santa_decode_flash(const santa_problem *p, const void *q, const void *k, con
                        workspace, workspace_bytes, stream);
 }
 
+int santa_decode_flash_sampler(const santa_problem *p, const void *q, const void *k, const void *v,
+                               int32_t S, int32_t sampler, const float *u, float *out,
+                               int32_t *sample_idx, int32_t *tile_budget, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    return run_sampled(SANTA_VARIANT_FLASH, p, q, k, v, S, sampler, u, out, sample_idx, tile_budget,
+                       workspace, workspace_bytes, stream);
+}
+
 int exact_decode_ref(const santa_problem *p, const void *q, const void *k, const void *v, float *out,
                      void *workspace, size_t workspace_bytes, void *stream) {
     Derived d;
@@ -235,6 +243,6 @@ const char *santa_status_string(int status) {
     }
 }
 
-int santa_abi_version(void) { return 2; }
+int santa_abi_version(void) { return 3; }
 
 }  // extern "C"

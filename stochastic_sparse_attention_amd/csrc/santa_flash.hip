@@ -20,6 +20,17 @@
 
 namespace santa {
 
+// #{m in [0, len) : th[m] < F} for a nondecreasing fp32 list
+__device__ __forceinline__ int count_below_f(const float *th, int len, float F) {
+    int lo = 0, hi = len;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (th[mid] < F) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
 // ===================================================================
 // S2ANTA-flash: tile kernel (score, local softmax, S_f local samples,
 // gather) -- merge below
@@ -28,14 +39,16 @@ namespace santa {
 // part_o [B, Hq, nt, d]: mean of the tile's S_f sampled V rows
 //
 // Local sampling per head (one wave): inclusive scan of the tile's weights,
-// local thresholds u_f + m/S_f on the local CDF P_j / Z_t with u_f = U * n_t,
-// and the same per-element count rule as pass 2 of prop (counts of
-// thresholds below each position, monotone, forced to S_f from the last
-// nonzero weight on).
-template <typename KV, int G, int T, bool PAGED>
+// local thresholds on the local CDF P_j / Z_t, and the same per-element count
+// rule as pass 2 of prop (counts of thresholds below each position, monotone,
+// forced to S_f from the last nonzero weight on).  Systematic thresholds
+// u_f + m/S_f (u_f = U * n_t) have closed-form counts; with LIST the S_f
+// thresholds of the tile, (m + u_m)/S_f or the tile's uniforms sorted, are
+// an LDS list searched by bisection.
+template <typename KV, int G, int T, bool PAGED, bool LIST>
 __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
     const typename QOf<KV>::type *__restrict__ q, const KV *__restrict__ k, const KV *__restrict__ v, KVLayout L,
-    int num_q_heads, int nt, int Sf, int S, float scale, const float *__restrict__ u,
+    int num_q_heads, int nt, int Sf, int S, int sampler, float scale, const float *__restrict__ u,
     float *__restrict__ part_m, float *__restrict__ part_z, float *__restrict__ part_o,
     int *__restrict__ sample_idx) {
     typedef typename ScorerFor<KV, G, T, PAGED>::type SC;
@@ -51,10 +64,12 @@ __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 
     // LDS: the scorer's staging area, then (after the barrier in tile_max)
-    // the tile's exp-weights E[G][T]
-    __shared__ __align__(16) unsigned char lds[cmax(SC::kStageVec * 16, G * T * 4)];
+    // the tile's exp-weights E[G][T] and, with LIST, the heads' local
+    // threshold lists TH[G][S_f <= T]
+    __shared__ __align__(16) unsigned char lds[cmax(SC::kStageVec * 16, (LIST ? 2 : 1) * G * T * 4)];
     __shared__ float red_m[kWavesPerBlock][16];
     float (*E)[T] = reinterpret_cast<float (*)[T]>(lds);
+    float (*TH)[T] = reinterpret_cast<float (*)[T]>(lds + (LIST ? G * T * 4 : 0));
 
     SC sc;
     sc.load_q(q + ((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim);
@@ -93,20 +108,76 @@ __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
         float excl = __shfl_up(lincl, 1);
         if (lane == 0) excl = 0.f;
         const float Zt = __shfl(lincl, 63);
-        const double uf = (double)u[bh] * (double)nt;
-        // per-element local threshold counts #{m : u_f + m/S_f < P_j / Z_t}
-        //   = ceil(P_j * a + b), a = S_f / Z_t, b = -u_f S_f (fp32; the
-        //   rounding moves a threshold by ~1e-7 of the tile's mass)
-        const float a = (float)((double)Sf / (double)Zt), bb = (float)(-uf * (double)Sf);
-        const float fSf = (float)Sf;
         int cj[EPL];
         int lmax = 0;
+        if constexpr (!LIST) {
+            const double uf = (double)u[bh] * (double)nt;
+            // per-element local threshold counts #{m : u_f + m/S_f < P_j / Z_t}
+            //   = ceil(P_j * a + b), a = S_f / Z_t, b = -u_f S_f (fp32; the
+            //   rounding moves a threshold by ~1e-7 of the tile's mass)
+            const float a = (float)((double)Sf / (double)Zt), bb = (float)(-uf * (double)Sf);
+            const float fSf = (float)Sf;
 #pragma unroll
-        for (int qq = 0; qq < EPL; ++qq) {
-            const int j = lane * EPL + qq;
-            const int cc = (int)fminf(fmaxf(ceilf(fmaf(excl + e[qq], a, bb)), 0.f), fSf);
-            lmax = max(lmax, j < lz ? cc : Sf);
-            cj[qq] = lmax;
+            for (int qq = 0; qq < EPL; ++qq) {
+                const int j = lane * EPL + qq;
+                const int cc = (int)fminf(fmaxf(ceilf(fmaf(excl + e[qq], a, bb)), 0.f), fSf);
+                lmax = max(lmax, j < lz ? cc : Sf);
+                cj[qq] = lmax;
+            }
+        } else {
+            // the tile's thresholds (uniforms tile-major: this tile's at
+            // t*S_f ..; outside [0,1) clamped into it, NaN as 0)
+            float *th = TH[hl];
+            const float *ub = u + (size_t)bh * S + (size_t)tile * Sf;
+            const float kBelowOne = 1.0f - 0x1p-24f;
+            constexpr int RMAX = T / 64;                 // S_f <= T: uniforms per lane
+            float uv[RMAX];
+#pragma unroll
+            for (int r = 0; r < RMAX; ++r) {
+                const int m = lane + 64 * r;
+                float x = m < Sf ? ub[m] : 0.f;
+                x = x >= 0.f ? x : 0.f;
+                uv[r] = x < kBelowOne ? x : kBelowOne;
+            }
+            if (sampler == kSamplerStrat) {
+                // (m + u_m)/S_f, formed in fp64, already in increasing order
+#pragma unroll
+                for (int r = 0; r < RMAX; ++r) {
+                    const int m = lane + 64 * r;
+                    if (m < Sf) th[m] = (float)(((double)m + (double)uv[r]) / (double)Sf);
+                }
+            } else {
+                // i.i.d.: rank of each uniform (ties by index), then placed
+#pragma unroll
+                for (int r = 0; r < RMAX; ++r)
+                    if (lane + 64 * r < Sf) th[lane + 64 * r] = uv[r];
+                wave_sync_lds();
+                int rank[RMAX];
+#pragma unroll
+                for (int r = 0; r < RMAX; ++r) rank[r] = 0;
+                for (int kk = 0; kk < Sf; ++kk) {
+                    const float o = th[kk];
+#pragma unroll
+                    for (int r = 0; r < RMAX; ++r) {
+                        const int m = lane + 64 * r;
+                        rank[r] += (o < uv[r] || (o == uv[r] && kk < m)) ? 1 : 0;
+                    }
+                }
+                wave_sync_lds();
+#pragma unroll
+                for (int r = 0; r < RMAX; ++r)
+                    if (lane + 64 * r < Sf) th[rank[r]] = uv[r];
+            }
+            wave_sync_lds();
+            // local CDF position P_j / Z_t against the list
+            const float invZt = 1.0f / Zt;
+#pragma unroll
+            for (int qq = 0; qq < EPL; ++qq) {
+                const int j = lane * EPL + qq;
+                const int cc = count_below_f(th, Sf, (excl + e[qq]) * invZt);
+                lmax = max(lmax, j < lz ? cc : Sf);
+                cj[qq] = lmax;
+            }
         }
         const int lmax_incl = wave_incl_max_scan(lmax, lane);
         int pmax = __shfl_up(lmax_incl, 1);
@@ -168,16 +239,21 @@ static hipError_t launch_flash_t(const LaunchArgs &a, const TimingHook &hook) {
     const int nt = a.max_nt;
     // with a timing hook the dispatch itself records the two events, so
     // they bracket the kernel's execution and nothing else
-    if (hook.begin)
-        hipExtLaunchKernelGGL((flash_tile_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * nt)), dim3(kBlock), 0, st, (hipEvent_t)hook.begin, (hipEvent_t)hook.end, 0,
-                       (const typename QOf<KV>::type *)a.q, (const KV *)a.k, (const KV *)a.v, L, a.num_q_heads, nt, a.S / nt,
-                       a.S, a.scale, a.u, (float *)a.ws.part_m, (float *)a.ws.part_l, (float *)a.ws.part_o,
-                       a.sample_idx);
-    else
-        hipLaunchKernelGGL((flash_tile_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * nt)), dim3(kBlock), 0, st,
-                       (const typename QOf<KV>::type *)a.q, (const KV *)a.k, (const KV *)a.v, L, a.num_q_heads, nt, a.S / nt,
-                       a.S, a.scale, a.u, (float *)a.ws.part_m, (float *)a.ws.part_l, (float *)a.ws.part_o,
-                       a.sample_idx);
+    auto launch = [&](auto kernel) {
+        if (hook.begin)
+            hipExtLaunchKernelGGL(kernel, dim3((unsigned)(a.batch * a.num_kv_heads * nt)), dim3(kBlock), 0, st,
+                                  (hipEvent_t)hook.begin, (hipEvent_t)hook.end, 0,
+                                  (const typename QOf<KV>::type *)a.q, (const KV *)a.k, (const KV *)a.v, L,
+                                  a.num_q_heads, nt, a.S / nt, a.S, a.sampler, a.scale, a.u, (float *)a.ws.part_m,
+                                  (float *)a.ws.part_l, (float *)a.ws.part_o, a.sample_idx);
+        else
+            hipLaunchKernelGGL(kernel, dim3((unsigned)(a.batch * a.num_kv_heads * nt)), dim3(kBlock), 0, st,
+                               (const typename QOf<KV>::type *)a.q, (const KV *)a.k, (const KV *)a.v, L,
+                               a.num_q_heads, nt, a.S / nt, a.S, a.sampler, a.scale, a.u, (float *)a.ws.part_m,
+                               (float *)a.ws.part_l, (float *)a.ws.part_o, a.sample_idx);
+    };
+    if (a.sampler == kSamplerSys) launch(flash_tile_kernel<KV, G, T, PAGED, false>);
+    else launch(flash_tile_kernel<KV, G, T, PAGED, true>);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(merge_tiles_kernel, dim3((unsigned)(a.batch * a.num_q_heads)), dim3(kMergeBlock),

@@ -44,14 +44,17 @@ def run_prop(dev, S, T=None, sampler="sys"):
     return out.cpu().numpy(), idx.cpu().numpy(), tb.cpu().numpy()
 
 
-def run_flash(dev, S):
+def run_flash(dev, S, sampler="sys"):
     torch = _torch()
     c = dev.inp.cfg
     BH = c.batch * c.num_q_heads
     out = torch.full((BH, c.head_dim), float("nan"), dtype=torch.float32, device=dev.q.device)
     idx = torch.full((BH, S), -7, dtype=torch.int32, device=dev.q.device)
     import stochastic_sparse_attention_amd as sa
-    sa.santa_decode_flash(dev.problem, dev.q, dev.k, dev.v, S, dev.u(S), out, idx)
+    if sampler == "sys":
+        sa.santa_decode_flash(dev.problem, dev.q, dev.k, dev.v, S, dev.u(S), out, idx)
+    else:
+        sa.santa_decode_flash_sampler(dev.problem, dev.q, dev.k, dev.v, S, sampler, dev.uniforms(S), out, idx)
     torch.cuda.synchronize()
     return out.cpu().numpy(), idx.cpu().numpy()
 
@@ -130,11 +133,14 @@ def check_prop(dev, S, repeat=True, sampler="sys"):
     return rep
 
 
-def check_flash(dev, S, repeat=True):
+def check_flash(dev, S, repeat=True, sampler="sys"):
     inp = dev.inp
-    out, idx = run_flash(dev, S)
+    out, idx = run_flash(dev, S, sampler)
     prob = oracle_problem(dev)
-    r = O.santa_flash(prob, inp.q, inp.k, inp.v, S, inp.u(S))
+    if sampler == "sys":
+        r = O.santa_flash(prob, inp.q, inp.k, inp.v, S, inp.u(S))
+    else:
+        r = O.santa_flash_sampler(prob, inp.q, inp.k, inp.v, S, sampler, inp.uniforms(S))
     rep = index_report(idx, r["idx"], r["delta"])
     assert rep["hard"] == 0, rep
     T = dev.problem.s.tile_len
@@ -146,7 +152,7 @@ def check_flash(dev, S, repeat=True):
     assert err <= OUT_TOL, err
     rep["max_abs_vs_replay"] = err
     if repeat:
-        out2, idx2 = run_flash(dev, S)
+        out2, idx2 = run_flash(dev, S, sampler)
         assert np.array_equal(idx, idx2)
         assert np.array_equal(out.view(np.uint32), out2.view(np.uint32))
     return rep

@@ -165,7 +165,7 @@ def test_empty_batch_is_a_noop(lib):
 def test_status_strings_and_version(lib):
     for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 12):
         assert isinstance(_lib.status_string(code), str) and _lib.status_string(code)
-    assert lib.santa_abi_version() >= 2
+    assert lib.santa_abi_version() >= 3
     assert lib.santa_set_timing_events(None, None) == OK
 
 

@@ -240,6 +240,20 @@ def test_flash_paged_uniform(gpu, kv):
     _say("prop paged uniform", kv, parity.check_prop(dev, 128, repeat=False))
 
 
+@pytest.mark.parametrize("sampler", ["strat", "iid"])
+@pytest.mark.parametrize("T,S", [(64, 4096), (256, 256), (256, 4096), (1024, 1024)])
+def test_flash_samplers(gpu, sampler, T, S):
+    """Stratified and i.i.d. local thresholds per tile: S_f = 64, 16, 256
+    (= T) and 256 at n = 4096; and a short last tile."""
+    import parity
+    cfg = synth.small_config(3, batch=2, seq_len=4096)
+    rep = parity.check_flash(_dev(cfg, 22, gpu, tile_len=T), S, sampler=sampler)
+    _say("flash", sampler, T, S, rep)
+    if T == 256 and S == 256:
+        cfg = synth.small_config(3, batch=1, seq_len=1000)      # 4 tiles, the last has 232 rows
+        _say("flash ragged", sampler, parity.check_flash(_dev(cfg, 23, gpu), 64, sampler=sampler))
+
+
 def test_flash_ragged_last_tile(gpu):
     import parity
     cfg = synth.small_config(3, batch=1, seq_len=1000)      # 4 tiles, last has 232 rows
