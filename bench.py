@@ -32,7 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attn µs/step + achieved HBM GB/s (% peak), 32k ctx, S=128, 1×MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-KERNEL_SOURCES = ["santa_prop.hip", "santa_flash.hip", "santa_exact.hip", "santa_kernels.h", "santa_score.h", "santa_device.h"]
+KERNEL_SOURCES = ["santa_prop.hip", "santa_prop_pass1.hip", "santa_flash.hip", "santa_exact.hip", "santa_kernels.h", "santa_score.h", "santa_device.h"]
 
 
 def kernel_source_hash():

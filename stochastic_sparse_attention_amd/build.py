@@ -12,7 +12,12 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsanta.so")
 ARCH = os.environ.get("SANTA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["santa_prop.hip", "santa_flash.hip", "santa_exact.hip", "santa_api.cpp"]
+# kernel sources, each compiled once per KV storage type (-DSANTA_KV=...)
+KV_SOURCES = ["santa_prop.hip", "santa_prop_pass1.hip", "santa_flash.hip", "santa_exact.hip"]
+KV_TYPES = {"bf16": "uint16_t", "fp8": "uint8_t", "f32": "float"}
+# host sources, compiled once
+HOST_SOURCES = ["santa_api.cpp", "santa_dispatch.cpp"]
+SOURCES = KV_SOURCES + HOST_SOURCES
 HEADERS = ["santa_device.h", "santa_score.h", "santa_launch.h", "santa_kernels.h"]
 
 COMMON = [
@@ -28,7 +33,7 @@ def _hipcc():
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose=False, jobs=4, out=None, defines=()):
+def build(verbose=False, jobs=None, out=None, defines=()):
     """Compile every source and link libsanta.so (or `out`).  `defines` adds
     preprocessor switches, e.g. ("SANTA_BF16_VALU",) builds the VALU scorer
     for bf16 instead of MFMA (used only for comparisons)."""
@@ -37,18 +42,23 @@ def build(verbose=False, jobs=4, out=None, defines=()):
     os.makedirs(objdir, exist_ok=True)
     dflags = [f"-D{d}" for d in defines]
 
-    def compile_one(src):
-        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        cmd = [_hipcc(), *COMMON, *dflags, "-c", os.path.join(CSRC, src), "-o", obj]
+    def compile_one(job):
+        src, kv = job
+        stem = os.path.splitext(src)[0] + ("." + kv if kv else "")
+        obj = os.path.join(objdir, stem + ".o")
+        extra = [f"-DSANTA_KV={KV_TYPES[kv]}"] if kv else []
+        cmd = [_hipcc(), *COMMON, *dflags, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+            raise RuntimeError(f"hipcc failed for {src} ({kv or 'host'}):\n{r.stderr}")
         return obj
 
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+    jobs_list = [(src, kv) for src in KV_SOURCES for kv in KV_TYPES] + [(src, None) for src in HOST_SOURCES]
+    workers = jobs or min(len(jobs_list), os.cpu_count() or 4, 16)
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = list(ex.map(compile_one, jobs_list))
     tmp = lib + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:

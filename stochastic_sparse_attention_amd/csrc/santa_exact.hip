@@ -179,6 +179,8 @@ static hipError_t launch_exact_t(const LaunchArgs &a, const TimingHook &hook) {
     return hipGetLastError();
 }
 
-hipError_t launch_exact(const LaunchArgs &a, const TimingHook &hook) { SANTA_DISPATCH(launch_exact_t) }
+template <typename KV>
+hipError_t launch_exact_kv(const LaunchArgs &a, const TimingHook &hook) { SANTA_G_CASES(KV, launch_exact_t) }
+SANTA_INSTANTIATE(launch_exact_kv)
 
 }  // namespace santa

@@ -263,6 +263,8 @@ static hipError_t launch_flash_t(const LaunchArgs &a, const TimingHook &hook) {
     return hipGetLastError();
 }
 
-hipError_t launch_flash(const LaunchArgs &a, const TimingHook &hook) { SANTA_DISPATCH(launch_flash_t) }
+template <typename KV>
+hipError_t launch_flash_kv(const LaunchArgs &a, const TimingHook &hook) { SANTA_G_CASES(KV, launch_flash_t) }
+SANTA_INSTANTIATE(launch_flash_kv)
 
 }  // namespace santa

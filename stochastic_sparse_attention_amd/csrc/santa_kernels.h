@@ -247,7 +247,7 @@ inline KVLayout layout_of(const LaunchArgs &a) {
     return KVLayout{a.num_kv_heads, a.max_seq_len, a.page_size, a.page_table, a.max_pages};
 }
 
-// dispatch over (dtype, group, tile length, layout)
+// dispatch over (group, tile length, layout) for one storage type
 #define SANTA_P_CASES(KV, G, T, FN) \
     return a.page_size ? FN<KV, G, T, true>(a, hook) : FN<KV, G, T, false>(a, hook);
 #define SANTA_T_CASES(KV, G, FN)                        \
@@ -267,9 +267,15 @@ inline KVLayout layout_of(const LaunchArgs &a) {
         case 8: SANTA_T_CASES(KV, 8, FN)                \
         default: return hipErrorInvalidValue;           \
     }
-#define SANTA_DISPATCH(FN)                                          \
-    if (a.kv_dtype == kKvBf16) { SANTA_G_CASES(uint16_t, FN) }      \
-    else if (a.kv_dtype == kKvFp8) { SANTA_G_CASES(uint8_t, FN) }   \
-    else { SANTA_G_CASES(float, FN) }
+// explicit instantiation of a per-type launcher for this compilation's KV
+// storage type (all three when SANTA_KV is not given)
+#ifdef SANTA_KV
+#define SANTA_INSTANTIATE(F) template hipError_t F<SANTA_KV>(const LaunchArgs &, const TimingHook &);
+#else
+#define SANTA_INSTANTIATE(F)                                                      \
+    template hipError_t F<uint16_t>(const LaunchArgs &, const TimingHook &);      \
+    template hipError_t F<uint8_t>(const LaunchArgs &, const TimingHook &);       \
+    template hipError_t F<float>(const LaunchArgs &, const TimingHook &);
+#endif
 
 }  // namespace santa

@@ -59,10 +59,17 @@ struct TimingHook {
     void *end;
 };
 
+// One decode call: the launches for a.kv_dtype (santa_dispatch.cpp).
 hipError_t launch_prop(const LaunchArgs &a, const TimingHook &hook);
 hipError_t launch_flash(const LaunchArgs &a, const TimingHook &hook);
 hipError_t launch_exact(const LaunchArgs &a, const TimingHook &hook);
-size_t visit_record_bytes();
-size_t prop_sample_lds_bytes(int kcap, int S, int sampler, int max_nt);
+
+// The launchers per KV storage type (uint16_t bf16, uint8_t e4m3, float).
+// Each kernel source is compiled once per type, and every compilation
+// instantiates only its own (SANTA_KV), so that they build in parallel.
+template <typename KV> hipError_t launch_prop_pass1_kv(const LaunchArgs &a, const TimingHook &hook);
+template <typename KV> hipError_t launch_prop_sample_kv(const LaunchArgs &a, const TimingHook &hook);
+template <typename KV> hipError_t launch_flash_kv(const LaunchArgs &a, const TimingHook &hook);
+template <typename KV> hipError_t launch_exact_kv(const LaunchArgs &a, const TimingHook &hook);
 
 }  // namespace santa
