@@ -16,6 +16,9 @@ namespace santa {
 #endif
 // above this many heads the systematic sampling kernel runs 8 waves per head
 constexpr int kSampleManyHeads = SANTA_SAMPLE_MANY_HEADS;
+// the same for the list generators, whose 16-wave workgroups take a whole
+// compute unit each (more registers)
+constexpr int kSampleListManyHeads = 256;
 constexpr int kMergeBlock = 1024;                  // threads of the per-head merge block
 constexpr int kMergeParts = kMergeBlock / kHeadDim;
 

@@ -92,7 +92,18 @@ struct SysCount {
 struct ListCount {
     const double *thr;    // [S], nondecreasing, in [0, 1)
     int S;
+    bool strat;           // thr[m] = (m + u_m)/S, i.e. thr[m] in [m/S, (m+1)/S)
     __device__ __forceinline__ int operator()(double C) const {
+        if (strat) {
+            // every threshold m <= k-2 is below C and every m >= k+2 is not,
+            // with k = floor(C S) (a margin of 1/S, far above the rounding
+            // of C S and of thr), so three comparisons give the exact count;
+            // the three reads are unconditional (clamped indices), so they
+            // are in flight together
+            const int k = (int)fmin(fmax(floor(C * (double)S), 0.0), (double)S);
+            const double a0 = thr[max(k - 1, 0)], a1 = thr[min(k, S - 1)], a2 = thr[min(k + 1, S - 1)];
+            return max(k - 1, 0) + (int)(k >= 1 && a0 < C) + (int)(k < S && a1 < C) + (int)(k + 1 < S && a2 < C);
+        }
         int lo = 0, hi = S;
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
@@ -112,20 +123,31 @@ struct ListCount {
 // them: lane l owns tiles [l*CH, l*CH + CH), CH = ceil(n_t/64)) held in
 // registers.  Writes the visit list, its length and the optional budgets.
 // The arithmetic and its order are those of the LDS variant below.
+constexpr int kStatRegs = kRegisterTiles / 64;   // tiles per reducer lane held in registers
+
+// the reducer lane's tile statistics (m_t, Z_t) for the register reducer,
+// (-inf, 0) past the lane's tiles; issued early so that their latency
+// overlaps other work
+__device__ __forceinline__ void load_lane_stats(const float2 *__restrict__ stp, int nt, int lane,
+                                                float2 (&st)[kStatRegs]) {
+    const int CH = (nt + 63) / 64;
+    const int tb = lane * CH;
+#pragma unroll
+    for (int i = 0; i < kStatRegs; ++i) {
+        const bool ok = i < CH && tb + i < nt;
+        st[i] = ok ? stp[tb + i] : make_float2(-INFINITY, 0.f);
+    }
+}
+
 template <int CHR, class CNT>
-__device__ __forceinline__ void reduce_in_registers(const float2 *__restrict__ stp, int nt, int lane, const CNT &count,
+__device__ __forceinline__ void reduce_in_registers(const float2 (&st)[kStatRegs], int nt, int lane, const CNT &count,
                                                     float scale, int kcap, VisitRec *vis,
                                                     int *__restrict__ budget, int max_nt, int &nvis_out) {
     const int CH = (nt + 63) / 64;
     const int tb = lane * CH;
-    float2 st[CHR];
     float lmaxv = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < CHR; ++i) {
-        const bool ok = i < CH && tb + i < nt;
-        st[i] = ok ? stp[tb + i] : make_float2(-INFINITY, 0.f);
-        lmaxv = fmaxf(lmaxv, st[i].x);
-    }
+    for (int i = 0; i < CHR; ++i) lmaxv = fmaxf(lmaxv, st[i].x);
     const float Mf = wave_max(lmaxv);
     // tile weight e^{scale (m_t - M)} in fp32: its rounding moves a tile's
     // CDF interval by ~1e-7 of the tile's own mass, and the same value is
@@ -146,15 +168,20 @@ __device__ __forceinline__ void reduce_in_registers(const float2 *__restrict__ s
     const double invZ = 1.0 / Z;
     double C[CHR];
     int c[CHR];
+    bool okv[CHR];
     double lrun = 0.0, clast = 0.0;
     int lcnt = 0;
 #pragma unroll
     for (int i = 0; i < CHR; ++i) {
-        const bool ok = i < CH && tb + i < nt;
-        if (ok) lrun += (double)st[i].y * f[i];
+        okv[i] = i < CH && tb + i < nt;
+        if (okv[i]) lrun += (double)st[i].y * f[i];
         C[i] = (tb + i == nt - 1) ? 1.0 : (excl + lrun) * invZ;
-        c[i] = ok ? count(C[i]) : 0;
-        if (ok) {
+    }
+#pragma unroll
+    for (int i = 0; i < CHR; ++i) c[i] = okv[i] ? count(C[i]) : 0;
+#pragma unroll
+    for (int i = 0; i < CHR; ++i) {
+        if (okv[i]) {
             lcnt = max(lcnt, c[i]);
             clast = C[i];
         }
@@ -296,16 +323,19 @@ __device__ __forceinline__ void reduce_with_lds(const float2 *__restrict__ stp, 
         for (int t = nt + lane; t < max_nt; t += 64) budget[t] = 0;
 }
 
+// st: the lane's statistics from load_lane_stats when nt <= kRegisterTiles
 template <class CNT>
-__device__ __forceinline__ void reduce_head(const float2 *__restrict__ stp, int nt, int lane, const CNT &count,
-                                            float scale, int kcap, VisitRec *vis, int *__restrict__ budget,
-                                            int max_nt, int &nvis_out, const ReducerLds &R) {
+__device__ __forceinline__ void reduce_head(const float2 *__restrict__ stp, const float2 (&st)[kStatRegs], int nt,
+                                            int lane, const CNT &count, float scale, int kcap, VisitRec *vis,
+                                            int *__restrict__ budget, int max_nt, int &nvis_out,
+                                            const ReducerLds &R) {
+    static_assert(kStatRegs == 4, "register reducer variants");
     if (nt <= 64)
-        reduce_in_registers<1>(stp, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out);
+        reduce_in_registers<1>(st, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out);
     else if (nt <= 128)
-        reduce_in_registers<2>(stp, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out);
+        reduce_in_registers<2>(st, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out);
     else if (nt <= kRegisterTiles)
-        reduce_in_registers<4>(stp, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out);
+        reduce_in_registers<4>(st, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out);
     else
         reduce_with_lds(stp, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out, R);
 }
@@ -321,13 +351,31 @@ __device__ __forceinline__ int count_below(const double *thr, int len, double F)
     return lo;
 }
 
-// at most 64 VGPRs (8 waves per SIMD), so that two of these 1024-thread
-// workgroups share a compute unit
+// #{m : thr[m] < F} clamped to [lo, hi], for the sorted list of S
+// thresholds; equal to lo + #{m in [lo, hi) : thr[m] < F} because the
+// thresholds below F form a prefix.  Stratified: the closed form of
+// ListCount; i.i.d.: a bisection over [lo, hi).
+__device__ __forceinline__ int count_in_range(const ListCount &lc, double F, int lo, int hi) {
+    if (lc.strat) return min(max(lc(F), lo), hi);
+    return lo + count_below(lc.thr + lo, hi - lo, F);
+}
+
+// the largest float at or below x, for x >= 0: the nearest float, one step
+// down if it lies above x (it is then > 0)
+__device__ __forceinline__ float float_at_or_below(double x) {
+    const float r = (float)x;
+    return (double)r > x ? __uint_as_float(__float_as_uint(r) - 1u) : r;
+}
+
+
 // LIST: stratified / i.i.d. thresholds (a sorted list in LDS); else the
 // systematic closed form
 // NW: waves per workgroup (16, or 8 for many heads: more heads per CU)
+// Registers: systematic, at most 64 VGPRs (8 waves per SIMD), so that two
+// 16-wave or four 8-wave workgroups share a compute unit; list generators,
+// at most 128 (4 waves per SIMD): one 16-wave or two 8-wave workgroups.
 template <typename KV, int T, bool PAGED, bool LIST, int NW>
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(8))) void prop_sample_kernel(
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(LIST ? 4 : 8))) void prop_sample_kernel(
     const KV *__restrict__ v, KVLayout L, const int *__restrict__ seq_lens, int batch, int num_q_heads,
     int G, int S, int max_nt, int kcap, int sampler, const float *__restrict__ u, float scale,
     const float *__restrict__ stash, const float2 *__restrict__ stats, float *__restrict__ out,
@@ -374,24 +422,74 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(8)))
         if (tid < kHeadDim) out[(size_t)bh * kHeadDim + tid] = 0.f;
         return;
     }
+    // the reducer's tile statistics, issued first so that their latency
+    // overlaps the threshold loads below
+    const float2 *stp = stats + (size_t)bh * max_nt;
+    float2 st[kStatRegs];
+    if (w == 0 && nt <= kRegisterTiles) load_lane_stats(stp, nt, lane, st);
+
     // ---------------- thresholds of the stratified and i.i.d. generators:
-    // (m + u_m)/S, or the uniforms sorted, in fp64 (inputs outside [0,1)
+    // (m + u_m)/S, or the uniforms sorted, in fp64 (uniforms outside [0,1)
     // are clamped into it; NaN counts as 0)
     if constexpr (LIST) {
         const float *ub = u + (size_t)bh * S;
         const double kBelowOne = 1.0 - 0x1p-53;
+        const double kUniformMax = 1.0 - 0x1p-24;      // the largest float below 1
+        // i.i.d. up to SB thresholds: the clamped uniforms are exact fp32
+        // values, ranked as fp32 keys held in the marker array (free until
+        // the reducer) and then placed into thr
+        const bool rank_sort = sampler == kSamplerIid && S <= SB;
+        float *keyf = reinterpret_cast<float *>(jsel);
         for (int m = tid; m < np; m += SB) {
             double x = INFINITY;                        // sort padding
             if (m < S) {
                 x = (double)ub[m];
-                x = x >= 0.0 ? x : 0.0;
+                x = x > 0.0 ? x : 0.0;                  // NaN and -0 become +0
+                x = x < kUniformMax ? x : kUniformMax;
                 if (sampler == kSamplerStrat) x = ((double)m + x) / (double)S;
                 x = x < kBelowOne ? x : kBelowOne;
             }
-            thr[m] = x;
+            if (rank_sort) {
+                if (m < S) keyf[m] = (float)x;
+            } else {
+                thr[m] = x;
+            }
         }
         __syncthreads();
-        if (sampler == kSamplerIid) {
+        if (rank_sort) {
+            // rank sort: threshold m goes to position #{j : x_j < x_m} +
+            // #{j < m : x_j == x_m}, i.e. the number of keys (bits of x_j,
+            // j) below (bits of x_m, m) as unsigned 64-bit integers (the
+            // order of nonnegative floats is that of their bits); P = SB/S
+            // (a power of two, at most 64) consecutive lanes share one
+            // threshold's comparisons
+            int P = 1;
+            while (P < 64 && 2 * P * S <= SB) P <<= 1;
+            const int m = tid / P, pp = tid % P;
+            float x = 0.f;
+            int rank = 0;
+            if (m < S) {
+                x = keyf[m];
+                const unsigned long long km = ((unsigned long long)__float_as_uint(x) << 32) | (unsigned)m;
+                // 8 reads in flight per batch (indices clamped, the extra
+                // ones masked out of the count), no branch per element
+                for (int j0 = pp; j0 < S; j0 += 8 * P) {
+                    float y[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) y[i] = keyf[min(j0 + i * P, S - 1)];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int j = j0 + i * P;
+                        const unsigned long long kj = ((unsigned long long)__float_as_uint(y[i]) << 32) | (unsigned)j;
+                        rank += (int)((j < S) & (kj < km));
+                    }
+                }
+            }
+            for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o);
+            // the keys are only read above and thr only written below
+            if (m < S && pp == 0) thr[rank] = (double)x;
+            __syncthreads();
+        } else if (sampler == kSamplerIid) {
             // bitonic sort of the np slots, ascending
             for (int k2 = 2; k2 <= np; k2 <<= 1) {
                 for (int j2 = k2 >> 1; j2 > 0; j2 >>= 1) {
@@ -417,13 +515,13 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(8)))
     if (w != 0) {
         for (int m = tid - kWave; m < S; m += SB - kWave) jsel[m] = -1;
     } else {
-        const float2 *stp = stats + (size_t)bh * max_nt;
         int *budget = tile_budget ? tile_budget + (size_t)bh * max_nt : nullptr;
         const ReducerLds R{tstat, tf, tC, tcn};
         if constexpr (!LIST)
-            reduce_head(stp, nt, lane, SysCount{(double)u[bh], S}, scale, kcap, vis, budget, max_nt, nvis_sh, R);
+            reduce_head(stp, st, nt, lane, SysCount{(double)u[bh], S}, scale, kcap, vis, budget, max_nt, nvis_sh, R);
         else
-            reduce_head(stp, nt, lane, ListCount{thr, S}, scale, kcap, vis, budget, max_nt, nvis_sh, R);
+            reduce_head(stp, st, nt, lane, ListCount{thr, S, sampler == kSamplerStrat}, scale, kcap, vis, budget,
+                        max_nt, nvis_sh, R);
     }
     __syncthreads();
     const int nvis = min(nvis_sh, kcap);
@@ -435,9 +533,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(8)))
     constexpr int EPL2 = T / LPT;
     const int sub = lane / LPT, gl = lane % LPT;          // tile slot in the wave, lane in group
     const int slot = lane >> 4, chunk = lane & 15;        // gather: row slot, 8-element chunk
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // V sums of the wave's 4 row slots
     // gather of the markers at positions [m_lo, m_hi), 64 at a time: they
     // are compacted into the wave's LDS list, then read 4 rows per wave
     // instruction with every load of a round in flight together; each row
@@ -465,13 +561,19 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(8)))
                     rows[u] = wrow[w][idx < nm ? idx : 0];
                     mul[u] = idx < nm ? wmul[w][idx] : 0.f;
                 }
-                float xv[kGatherRounds][8];
-#pragma unroll
-                for (int u = 0; u < kGatherRounds; ++u) load_v8<KV>(v + row_offset(L, b, g, rows[u]) + 8 * chunk, xv[u]);
+                // every load of the batch in flight as raw storage, each
+                // widened only when it is added
+                Raw8<KV> raw[kGatherRounds];
 #pragma unroll
                 for (int u = 0; u < kGatherRounds; ++u)
+                    raw[u] = load_raw8<KV>(v + row_offset(L, b, g, rows[u]) + 8 * chunk);
 #pragma unroll
-                    for (int e2 = 0; e2 < 8; ++e2) acc[e2] = fmaf(mul[u], xv[u][e2], acc[e2]);
+                for (int u = 0; u < kGatherRounds; ++u) {
+                    float xv[8];
+                    widen8(raw[u], xv);
+#pragma unroll
+                    for (int e2 = 0; e2 < 8; ++e2) acc[e2] = fmaf(mul[u], xv[e2], acc[e2]);
+                }
             }
             wave_sync_lds();
         }
@@ -503,7 +605,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(8)))
         // count reached at the lane's last token: systematic, the closed
         // form; stratified / i.i.d., a bisection over the tile's thresholds
         // at the CDF position P a + b
-        const int yl = list ? lo + count_below(thr + lo, hi - lo, (double)fmaf(e[EPL2 - 1], rec.a, bl))
+        const ListCount lcnt{thr, S, sampler == kSamplerStrat};
+        const int yl = list ? count_in_range(lcnt, (double)fmaf(e[EPL2 - 1], rec.a, bl), lo, hi)
                             : max((int)fminf(ceilf(fmaf(e[EPL2 - 1], rec.a, bl)), fhi), lo);
         const int gmax = group_incl_max<LPT>(yl);
         int prev = __shfl_up(gmax, 1);                     // count reached by the earlier lanes
@@ -526,16 +629,23 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(8)))
                     }
                 }
             } else {
-                // merge of the lane's tokens with its thresholds
+                // merge of the lane's tokens with its thresholds.  The next
+                // threshold is kept in a register as the largest float at
+                // or below it: for a float F, thr < F exactly when that
+                // float is < F, so the test is the fp64 one.  A token past
+                // it reaches clamp(#{thr < F}, yp + 1, yl): one closed-form
+                // count (stratified) or one bisection (i.i.d.) per token that
+                // holds thresholds, however many it holds.
+                float nxt = float_at_or_below(thr[yp]);     // yp < yl <= S here
 #pragma unroll
                 for (int qq = 0; qq < EPL2; ++qq) {
-                    const double Fq = (double)fmaf(e[qq], rec.a, bl);
-                    int y = yp;
-                    while (y < yl && thr[y] < Fq) ++y;
-                    if (y > yp) {
+                    const float Fq = fmaf(e[qq], rec.a, bl);
+                    if (nxt < Fq) {
+                        const int y = count_in_range(lcnt, (double)Fq, yp + 1, yl);
                         jsel[yp] = min(start + gl * EPL2 + qq, n - 1);
                         jmul[yp] = y - yp;
                         yp = y;
+                        nxt = yp < yl ? float_at_or_below(thr[yp]) : INFINITY;
                     }
                 }
             }
@@ -618,10 +728,9 @@ static hipError_t launch_sample_t(const LaunchArgs &a, const TimingHook &) {
     const KVLayout L = layout_of(a);
     const int BH = a.batch * a.num_q_heads;
     const size_t lds = prop_sample_lds_bytes(a.kmax, a.S, a.sampler, max_nt);
-    // few heads: 16 waves per head; many heads (systematic thresholds): 8,
-    // so that more heads (and their dependent memory round trips) share
-    // each compute unit
-    const bool many = BH > kSampleManyHeads && a.sampler == kSamplerSys;
+    // few heads: 16 waves per head; many heads: 8, so that more heads (and
+    // their dependent memory round trips) share each compute unit
+    const bool many = BH > (a.sampler == kSamplerSys ? kSampleManyHeads : kSampleListManyHeads);
     auto launch = [&](auto kernel, int nw) -> hipError_t {
         if (lds > 64 * 1024) {
             const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
@@ -633,7 +742,9 @@ static hipError_t launch_sample_t(const LaunchArgs &a, const TimingHook &) {
                            (const float *)stash, (const float2 *)stats, a.out, a.sample_idx, a.tile_budget);
         return hipGetLastError();
     };
-    if (a.sampler != kSamplerSys) return launch(prop_sample_kernel<KV, T, PAGED, true, 16>, 16);
+    if (a.sampler != kSamplerSys)
+        return many ? launch(prop_sample_kernel<KV, T, PAGED, true, 8>, 8)
+                    : launch(prop_sample_kernel<KV, T, PAGED, true, 16>, 16);
     if (many) return launch(prop_sample_kernel<KV, T, PAGED, false, 8>, 8);
     return launch(prop_sample_kernel<KV, T, PAGED, false, 16>, 16);
 }

@@ -25,7 +25,7 @@ def _torch():
     return torch
 
 
-def run_prop(dev, S, T=None, sampler="sys"):
+def run_prop(dev, S, T=None, sampler="sys", uniforms=None):
     torch = _torch()
     c = dev.inp.cfg
     BH = c.batch * c.num_q_heads
@@ -38,8 +38,8 @@ def run_prop(dev, S, T=None, sampler="sys"):
     if sampler == "sys":
         sa.santa_decode_prop(dev.problem, dev.q, dev.k, dev.v, S, dev.u(S), out, idx, tb)
     else:
-        sa.santa_decode_prop_sampler(dev.problem, dev.q, dev.k, dev.v, S, sampler, dev.uniforms(S),
-                                     out, idx, tb)
+        uu = dev.uniforms(S) if uniforms is None else torch.from_numpy(uniforms).to(dev.q.device)
+        sa.santa_decode_prop_sampler(dev.problem, dev.q, dev.k, dev.v, S, sampler, uu, out, idx, tb)
     torch.cuda.synchronize()
     return out.cpu().numpy(), idx.cpu().numpy(), tb.cpu().numpy()
 
@@ -90,18 +90,21 @@ def index_report(gpu_idx, ora_idx, delta):
             "near_edges": int((delta < BOUNDARY_EXEMPT).sum())}
 
 
-def check_prop(dev, S, repeat=True, sampler="sys"):
+def check_prop(dev, S, repeat=True, sampler="sys", uniforms=None, oracle_uniforms=None):
     """Run prop on the GPU (systematic, stratified or i.i.d. thresholds) and
-    hold it to the bar; returns a report dict."""
+    hold it to the bar; returns a report dict.  `uniforms` replaces the
+    seeded [B*Hq, S] uniforms of the list generators; the oracle gets
+    `oracle_uniforms` if given (e.g. the same values clamped), else the same."""
     inp = dev.inp
     c = inp.cfg
     T = dev.problem.s.tile_len
-    out, idx, tb = run_prop(dev, S, sampler=sampler)
+    out, idx, tb = run_prop(dev, S, sampler=sampler, uniforms=uniforms)
     prob = oracle_problem(dev)
     if sampler == "sys":
         r = O.santa_prop(prob, inp.q, inp.k, inp.v, S, inp.u(S))
     else:
-        r = O.santa_prop_sampler(prob, inp.q, inp.k, inp.v, S, sampler, inp.uniforms(S))
+        ou = oracle_uniforms if oracle_uniforms is not None else uniforms
+        r = O.santa_prop_sampler(prob, inp.q, inp.k, inp.v, S, sampler, inp.uniforms(S) if ou is None else ou)
     rep = index_report(idx, r["idx"], r["delta"])
     assert rep["hard"] == 0, rep
     # budgets: sum to S (or 0 for empty requests), match the GPU's own indices
@@ -127,7 +130,7 @@ def check_prop(dev, S, repeat=True, sampler="sys"):
     rep["max_abs_vs_replay"] = err
     rep["max_abs_vs_oracle_estimate"] = float(np.max(np.abs(out - r["out"])))
     if repeat:
-        out2, idx2, tb2 = run_prop(dev, S, sampler=sampler)
+        out2, idx2, tb2 = run_prop(dev, S, sampler=sampler, uniforms=uniforms)
         assert np.array_equal(idx, idx2) and np.array_equal(tb, tb2)
         assert np.array_equal(out.view(np.uint32), out2.view(np.uint32))
     return rep

@@ -86,6 +86,30 @@ def test_prop_samplers_ragged_paged_many_tiles(gpu, sampler):
     _say(sampler, "313 tiles", rep)
 
 
+@pytest.mark.parametrize("S", [128, 1000, 1024, 1500])
+def test_prop_list_ties_and_clamping(gpu, S):
+    """i.i.d. thresholds with many equal uniforms (the device sorts by rank
+    up to S = 1024, with a bitonic network above), and uniforms outside
+    [0, 1) for both list generators: the device clamps them into [0, 1)
+    (NaN counts as 0), so its result is the oracle's on the clamped values."""
+    import parity
+    cfg = synth.small_config(2, batch=1, seq_len=3000, num_q_heads=8, num_kv_heads=2)
+    dev = _dev(cfg, 30, gpu)
+    rng = np.random.default_rng(S)
+    vals = (rng.integers(0, 2 ** 24, 6) * 2.0 ** -24).astype(np.float32)
+    u = vals[rng.integers(0, 6, (8, S))]
+    _say("iid, 6 distinct uniforms, S", S, parity.check_prop(dev, S, sampler="iid", uniforms=u))
+    raw = u.copy()
+    raw[:, ::7] = 1.5
+    raw[:, 3::11] = -0.25
+    raw[:, 5::13] = np.nan
+    raw[:, 6::17] = 1.0
+    clamped = np.clip(np.nan_to_num(raw, nan=0.0), 0.0, np.float32(1.0 - 2.0 ** -24)).astype(np.float32)
+    for smp in ("strat", "iid"):
+        _say(smp, "clamped, S", S, parity.check_prop(dev, S, sampler=smp, uniforms=raw, oracle_uniforms=clamped,
+                                                     repeat=False))
+
+
 def test_sampler_variance_ordering(gpu):
     """key design 1 / Table 2 structure, on the GPU path: over many draws of
     the random inputs, the systematic and stratified estimators have lower
@@ -129,6 +153,18 @@ def test_prop_many_heads(gpu):
     dev = _dev(cfg, 19, gpu)
     _say("768 heads, S=128", parity.check_prop(dev, 128))
     _say("768 heads, S=1000", parity.check_prop(dev, 1000, repeat=False))
+
+
+@pytest.mark.parametrize("sampler", ["strat", "iid"])
+def test_prop_list_many_heads(gpu, sampler):
+    """More than 256 heads: the list generators run 8 waves per head (512
+    threads: the i.i.d. rank sort up to S = 512, the bitonic network above).
+    Mixed lengths, paged KV."""
+    import parity
+    cfg = synth.small_config(5, batch=24, seq_len=2500, min_seq_len=64)
+    dev = _dev(cfg, 21, gpu)
+    for S in (128, 1000):
+        _say(sampler, "768 heads, S", S, parity.check_prop(dev, S, sampler=sampler, repeat=S == 128))
 
 
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (32, 8), (16, 2)])
