@@ -32,7 +32,9 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attn µs/step + achieved HBM GB/s (% peak), 32k ctx, S=128, 1×MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-KERNEL_SOURCES = ["santa_prop.hip", "santa_prop_pass1.hip", "santa_flash.hip", "santa_exact.hip", "santa_kernels.h", "santa_score.h", "santa_device.h"]
+# the sources of the dominant kernel (prop pass 1), whose HBM counters
+# profiles/traffic.json holds
+KERNEL_SOURCES = ["santa_prop_pass1.hip", "santa_kernels.h", "santa_score.h", "santa_device.h", "santa_launch.h"]
 
 
 def kernel_source_hash():
@@ -43,15 +45,16 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel_key):
+def read_traffic(kernel_key, cid):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
-    was taken on the current kernel sources (else None)."""
+    was taken on the current kernel sources and on workload `cid` (else
+    None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_hash") != kernel_source_hash():
+    if t.get("source_hash") != kernel_source_hash() or t.get("config_id") != cid:
         return None
     e = t.get("kernels", {}).get(kernel_key)
     return None if e is None else e.get("bytes_per_launch")
@@ -335,7 +338,7 @@ def main(argv=None):
         "tiles_visited_per_head": round(float((tb_np > 0).sum(1).mean()), 2),
         "roofline": {"kernel": "prop_pass1_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": read_traffic("prop_pass1_kernel"),
+                     "traffic": read_traffic("prop_pass1_kernel", cfg.cid),
                      "bytes_per_launch": pass1_bytes, "avg_launch_us": round(kern_ms * 1e3, 3),
                      "launch_us_p10_p50_p90": [round(float(np.percentile(kern_sorted, q)) * 1e3, 3)
                                                for q in (10, 50, 90)],

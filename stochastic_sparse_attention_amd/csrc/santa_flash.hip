@@ -21,14 +21,23 @@
 namespace santa {
 
 // #{m in [0, len) : th[m] < F} for a nondecreasing fp32 list
-__device__ __forceinline__ int count_below_f(const float *th, int len, float F) {
-    int lo = 0, hi = len;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (th[mid] < F) lo = mid + 1;
-        else hi = mid;
+// c[i] = #{m < len : th[m] < F[i]} for a nondecreasing list, the N searches
+// in lockstep (binary lifting: c grows by each power of two, largest first,
+// while th[c + step - 1] < F), so that their LDS reads are in flight together
+template <int N>
+__device__ __forceinline__ void count_below_f(const float *th, int len, const float (&F)[N], int (&c)[N]) {
+    int step = 1;
+    while (2 * step <= len) step <<= 1;
+#pragma unroll
+    for (int i = 0; i < N; ++i) c[i] = 0;
+    for (; step > 0; step >>= 1) {
+        float o[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) o[i] = th[min(c[i] + step, len) - 1];
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if (c[i] + step <= len && o[i] < F[i]) c[i] += step;
     }
-    return lo;
 }
 
 // ===================================================================
@@ -70,6 +79,26 @@ __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
     __shared__ float red_m[kWavesPerBlock][16];
     float (*E)[T] = reinterpret_cast<float (*)[T]>(lds);
     float (*TH)[T] = reinterpret_cast<float (*)[T]>(lds + (LIST ? G * T * 4 : 0));
+
+    // list generators: a head's uniforms for this tile (tile-major: this
+    // tile's at t*S_f ..), outside [0,1) clamped into it (NaN and -0 as +0).
+    // With one head per wave they are loaded before K, so that their
+    // latency overlaps the K stream.
+    constexpr int RMAX = T / 64;                         // S_f <= T: uniforms per lane
+    constexpr bool kEarlyU = LIST && G <= kWavesPerBlock;
+    auto load_uniforms = [&](int hl, float (&uvo)[RMAX]) {
+        const float kBelowOne = 1.0f - 0x1p-24f;
+        const float *ub = u + ((size_t)b * num_q_heads + (size_t)g * G + hl) * S + (size_t)tile * Sf;
+#pragma unroll
+        for (int r = 0; r < RMAX; ++r) {
+            const int m = lane + 64 * r;
+            float x = m < Sf ? ub[m] : 0.f;
+            x = x > 0.f ? x : 0.f;
+            uvo[r] = x < kBelowOne ? x : kBelowOne;
+        }
+    };
+    float uv_early[RMAX];
+    if constexpr (kEarlyU) load_uniforms(w < G ? w : G - 1, uv_early);   // waves past G: unused
 
     SC sc;
     sc.load_q(q + ((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim);
@@ -128,16 +157,12 @@ __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
             // the tile's thresholds (uniforms tile-major: this tile's at
             // t*S_f ..; outside [0,1) clamped into it, NaN as 0)
             float *th = TH[hl];
-            const float *ub = u + (size_t)bh * S + (size_t)tile * Sf;
-            const float kBelowOne = 1.0f - 0x1p-24f;
-            constexpr int RMAX = T / 64;                 // S_f <= T: uniforms per lane
             float uv[RMAX];
+            if constexpr (kEarlyU) {
 #pragma unroll
-            for (int r = 0; r < RMAX; ++r) {
-                const int m = lane + 64 * r;
-                float x = m < Sf ? ub[m] : 0.f;
-                x = x >= 0.f ? x : 0.f;
-                uv[r] = x < kBelowOne ? x : kBelowOne;
+                for (int r = 0; r < RMAX; ++r) uv[r] = uv_early[r];
+            } else {
+                load_uniforms(hl, uv);
             }
             if (sampler == kSamplerStrat) {
                 // (m + u_m)/S_f, formed in fp64, already in increasing order
@@ -152,15 +177,25 @@ __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
                 for (int r = 0; r < RMAX; ++r)
                     if (lane + 64 * r < Sf) th[lane + 64 * r] = uv[r];
                 wave_sync_lds();
+                // rank: the number of keys (bits of u_k, k) below (bits of
+                // u_m, m) as unsigned 64-bit integers (nonnegative floats
+                // order as their bits); 8 reads in flight, no branches
                 int rank[RMAX];
+                unsigned long long km[RMAX];
 #pragma unroll
-                for (int r = 0; r < RMAX; ++r) rank[r] = 0;
-                for (int kk = 0; kk < Sf; ++kk) {
-                    const float o = th[kk];
+                for (int r = 0; r < RMAX; ++r) {
+                    rank[r] = 0;
+                    km[r] = ((unsigned long long)__float_as_uint(uv[r]) << 32) | (unsigned)(lane + 64 * r);
+                }
+                for (int k0 = 0; k0 < Sf; k0 += 8) {
+                    float o[8];
 #pragma unroll
-                    for (int r = 0; r < RMAX; ++r) {
-                        const int m = lane + 64 * r;
-                        rank[r] += (o < uv[r] || (o == uv[r] && kk < m)) ? 1 : 0;
+                    for (int i = 0; i < 8; ++i) o[i] = th[min(k0 + i, Sf - 1)];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const unsigned long long ko = ((unsigned long long)__float_as_uint(o[i]) << 32) | (unsigned)(k0 + i);
+#pragma unroll
+                        for (int r = 0; r < RMAX; ++r) rank[r] += (int)((k0 + i < Sf) & (ko < km[r]));
                     }
                 }
                 wave_sync_lds();
@@ -171,11 +206,15 @@ __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
             wave_sync_lds();
             // local CDF position P_j / Z_t against the list
             const float invZt = 1.0f / Zt;
+            float F[EPL];
+            int cc[EPL];
+#pragma unroll
+            for (int qq = 0; qq < EPL; ++qq) F[qq] = (excl + e[qq]) * invZt;
+            count_below_f(th, Sf, F, cc);
 #pragma unroll
             for (int qq = 0; qq < EPL; ++qq) {
                 const int j = lane * EPL + qq;
-                const int cc = count_below_f(th, Sf, (excl + e[qq]) * invZt);
-                lmax = max(lmax, j < lz ? cc : Sf);
+                lmax = max(lmax, j < lz ? cc[qq] : Sf);
                 cj[qq] = lmax;
             }
         }
