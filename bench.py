@@ -240,9 +240,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the decode path runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
-        log("bench.py: only single-GPU runs are supported (the path is not sharded in this build)")
+        log("bench.py: only single-GPU runs are supported (the decode path is not sharded across GPUs)")
         return 2
 
     import torch
