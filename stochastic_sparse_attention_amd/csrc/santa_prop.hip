@@ -1,5 +1,6 @@
 // santa_prop.hip -- S2ANTA-prop: reducer + pass 2 (the per-head sampling kernel)
-// and the launcher of the whole prop step (pass 1 is in santa_prop_pass1.hip).
+// and its launcher.  Pass 1 is in santa_prop_pass1.hip; santa_dispatch.cpp
+// launches the two in order.
 //
 // The method follows the web page "Stochastic Sparse Attention for
 // Memory-Bound Inference" (ICML 2026 paper notes on SANTA):
@@ -16,30 +17,32 @@
 // Precision plan (why index parity with an fp64 oracle holds): scores are
 // accumulated unscaled (bf16 products are exact in fp32; fp32 inputs use
 // fp64), the tile max is subtracted before the scale is applied, the reducer
-// works in fp64, and the CDF positions of pass 2 are formed in fp64.
+// works in fp64, and pass 2 evaluates each CDF position as one fp32 fma
+// whose coefficients were formed in fp64.
 #include "santa_kernels.h"
 
 namespace santa {
 
 // ===================================================================
-// S2ANTA-prop, reducer + pass 2: one 1024-thread workgroup per (request,
-// q head).  No cross-workgroup communication.
+// S2ANTA-prop, reducer + pass 2: one workgroup per (request, q head), of
+// 16 waves (8 with many heads).  No cross-workgroup communication.
 // ===================================================================
-// Reducer (thread t <-> tile t; n_t <= 1024): global max M of the tile
-// maxima, tile masses z_t = Z_t e^{scale (m_t - M)}, Z = sum z_t, tile CDF
-// C_t (fp64, C_{n_t-1} := 1), threshold counts cnt_t = #{m : U + m/S < C_t}
-// made monotone, budgets S_t = cnt_t - cnt_{t-1}; tiles with S_t > 0 go to
-// an LDS visit list in tile order.
+// Reducer (wave 0; lane l owns tiles [l CH, l CH + CH), CH = ceil(n_t/64),
+// n_t <= 1024): global max M of the tile maxima, tile masses
+// z_t = Z_t e^{scale (m_t - M)}, Z = sum z_t, tile CDF C_t (fp64,
+// C_{n_t-1} := 1), threshold counts cnt_t = #{thresholds < C_t} made
+// monotone, budgets S_t = cnt_t - cnt_{t-1}; tiles with S_t > 0 go to an LDS
+// visit list in tile order.
 // Pass 2 (LPT lanes per visited tile, EPL consecutive tokens per lane):
-// inclusive scan of the tile's stash P_j, then the count of thresholds below
-// the CDF position of token j, c_j = ceil(P_j a + b) clamped to the tile's
-// threshold range (see VisitRec).  Token j takes thresholds c_{j-1} ..
-// c_j - 1, so only the tokens where the count steps are recorded: a marker
-// (row j, multiplicity c_j - c_{j-1}) at LDS position c_{j-1}.  If the fp32
-// tile total falls short of the tile's last threshold, the remaining ones go
-// to the last token of nonzero weight, as a marker at the short count.
-// Every threshold position holds the marker of its token or lies after it
-// in the same tile, so a running max over positions gives the index list.
+// inclusive scan of the tile's stash P_j, then the count c_j of thresholds
+// below the CDF position of token j, clamped to the tile's threshold range
+// (see VisitRec).  Token j takes thresholds c_{j-1} .. c_j - 1, so only the
+// tokens where the count steps are recorded: a marker (row j, multiplicity
+// c_j - c_{j-1}) at LDS position c_{j-1}.  If the fp32 tile total falls short
+// of the tile's last threshold, the remaining ones go to the last token of
+// nonzero weight, as a marker at the short count.  Every threshold position
+// holds the marker of its token or lies after it in the same tile, so a
+// running max over positions gives the index list.
 // Gather: each wave reads the V rows of its own tiles' markers right away
 // (16 lanes per row, 4 rows per wave instruction) and accumulates
 // multiplicity * row; the waves' sums are added in a fixed order and
