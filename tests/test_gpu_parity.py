@@ -358,9 +358,10 @@ def test_full_size_prop(gpu, cid):
 
 # ------------------------------------------------- HIP graph replay
 def test_graph_replays_match_eager(gpu):
-    """prop (all three threshold generators) and exact decode captured in one
-    HIP graph: every replay, with eager work and synchronisations in
-    between, gives results bitwise equal to the eager calls."""
+    """prop (all three threshold generators), flash (systematic and
+    stratified) and exact decode captured in one HIP graph: every replay,
+    with eager work and synchronisations in between, gives results bitwise
+    equal to the eager calls."""
     import torch
     import stochastic_sparse_attention_amd as sa
     cfg = synth.small_config(2, batch=2, seq_len=3000)
@@ -370,7 +371,11 @@ def test_graph_replays_match_eager(gpu):
     U, uu = dev.u(S), dev.uniforms(S)
     ws = torch.empty(sa.santa_workspace_size(dev.problem, "prop", S), dtype=torch.uint8, device=gpu)
     wse = torch.empty(sa.santa_workspace_size(dev.problem, "exact"), dtype=torch.uint8, device=gpu)
-    outs = {k: torch.empty((BH, 128), dtype=torch.float32, device=gpu) for k in ("sys", "strat", "iid", "exact")}
+    SF = 16 * max_nt                                  # flash: 16 samples per tile
+    UF, uuf = dev.u(SF), dev.uniforms(SF)
+    wsf = torch.empty(sa.santa_workspace_size(dev.problem, "flash", SF), dtype=torch.uint8, device=gpu)
+    outs = {k: torch.empty((BH, 128), dtype=torch.float32, device=gpu)
+            for k in ("sys", "strat", "iid", "exact", "flash", "flash_strat")}
     idx = torch.empty((BH, S), dtype=torch.int32, device=gpu)
     tb = torch.empty((BH, max_nt), dtype=torch.int32, device=gpu)
 
@@ -379,6 +384,9 @@ def test_graph_replays_match_eager(gpu):
         for smp in ("strat", "iid"):
             sa.santa_decode_prop_sampler(dev.problem, dev.q, dev.k, dev.v, S, smp, uu, outs[smp], workspace=ws)
         sa.exact_decode_ref(dev.problem, dev.q, dev.k, dev.v, outs["exact"], workspace=wse)
+        sa.santa_decode_flash(dev.problem, dev.q, dev.k, dev.v, SF, UF, outs["flash"], workspace=wsf)
+        sa.santa_decode_flash_sampler(dev.problem, dev.q, dev.k, dev.v, SF, "strat", uuf, outs["flash_strat"],
+                                      workspace=wsf)
 
     step()
     torch.cuda.synchronize()
