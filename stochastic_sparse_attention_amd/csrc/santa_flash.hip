@@ -82,10 +82,9 @@ __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
 
     // list generators: a head's uniforms for this tile (tile-major: this
     // tile's at t*S_f ..), outside [0,1) clamped into it (NaN and -0 as +0).
-    // With one head per wave they are loaded before K, so that their
-    // latency overlaps the K stream.
+    // (Loading them before K was measured: the registers held through the
+    // scorer cost a wave per SIMD, more than the overlap gained.)
     constexpr int RMAX = T / 64;                         // S_f <= T: uniforms per lane
-    constexpr bool kEarlyU = LIST && G <= kWavesPerBlock;
     auto load_uniforms = [&](int hl, float (&uvo)[RMAX]) {
         const float kBelowOne = 1.0f - 0x1p-24f;
         const float *ub = u + ((size_t)b * num_q_heads + (size_t)g * G + hl) * S + (size_t)tile * Sf;
@@ -97,8 +96,6 @@ __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
             uvo[r] = x < kBelowOne ? x : kBelowOne;
         }
     };
-    float uv_early[RMAX];
-    if constexpr (kEarlyU) load_uniforms(w < G ? w : G - 1, uv_early);   // waves past G: unused
 
     SC sc;
     sc.load_q(q + ((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim);
@@ -158,59 +155,85 @@ __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
             // t*S_f ..; outside [0,1) clamped into it, NaN as 0)
             float *th = TH[hl];
             float uv[RMAX];
-            if constexpr (kEarlyU) {
-#pragma unroll
-                for (int r = 0; r < RMAX; ++r) uv[r] = uv_early[r];
-            } else {
-                load_uniforms(hl, uv);
-            }
-            if (sampler == kSamplerStrat) {
-                // (m + u_m)/S_f, formed in fp64, already in increasing order
-#pragma unroll
-                for (int r = 0; r < RMAX; ++r) {
-                    const int m = lane + 64 * r;
-                    if (m < Sf) th[m] = (float)(((double)m + (double)uv[r]) / (double)Sf);
-                }
-            } else {
-                // i.i.d.: rank of each uniform (ties by index), then placed
-#pragma unroll
-                for (int r = 0; r < RMAX; ++r)
-                    if (lane + 64 * r < Sf) th[lane + 64 * r] = uv[r];
-                wave_sync_lds();
-                // rank: the number of keys (bits of u_k, k) below (bits of
-                // u_m, m) as unsigned 64-bit integers (nonnegative floats
-                // order as their bits); 8 reads in flight, no branches
-                int rank[RMAX];
-                unsigned long long km[RMAX];
-#pragma unroll
-                for (int r = 0; r < RMAX; ++r) {
-                    rank[r] = 0;
-                    km[r] = ((unsigned long long)__float_as_uint(uv[r]) << 32) | (unsigned)(lane + 64 * r);
-                }
-                for (int k0 = 0; k0 < Sf; k0 += 8) {
-                    float o[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) o[i] = th[min(k0 + i, Sf - 1)];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const unsigned long long ko = ((unsigned long long)__float_as_uint(o[i]) << 32) | (unsigned)(k0 + i);
-#pragma unroll
-                        for (int r = 0; r < RMAX; ++r) rank[r] += (int)((k0 + i < Sf) & (ko < km[r]));
-                    }
-                }
-                wave_sync_lds();
-#pragma unroll
-                for (int r = 0; r < RMAX; ++r)
-                    if (lane + 64 * r < Sf) th[rank[r]] = uv[r];
-            }
-            wave_sync_lds();
-            // local CDF position P_j / Z_t against the list
+            load_uniforms(hl, uv);
+            // local CDF positions P_j / Z_t
             const float invZt = 1.0f / Zt;
             float F[EPL];
             int cc[EPL];
 #pragma unroll
             for (int qq = 0; qq < EPL; ++qq) F[qq] = (excl + e[qq]) * invZt;
-            count_below_f(th, Sf, F, cc);
+            // counts c = #{thresholds < F}, with no chain of dependent LDS
+            // reads: LDS is shared with the other workgroups' K staging, so
+            // each dependent read waits long
+            if (sampler == kSamplerIid && Sf <= 64) {
+                // i.i.d., short list: the count does not depend on the order,
+                // so lane m keeps u_m and every lane compares its positions
+                // with each u_m in turn (read across the wave); no sort
+#pragma unroll
+                for (int qq = 0; qq < EPL; ++qq) cc[qq] = 0;
+                const int ub = __float_as_int(uv[0]);
+                for (int m = 0; m < Sf; ++m) {
+                    const float t = __int_as_float(__builtin_amdgcn_readlane(ub, m));
+#pragma unroll
+                    for (int qq = 0; qq < EPL; ++qq) cc[qq] += (int)(t < F[qq]);
+                }
+            } else {
+                if (sampler == kSamplerStrat) {
+                    // (m + u_m)/S_f, formed in fp64, already in increasing order
+#pragma unroll
+                    for (int r = 0; r < RMAX; ++r) {
+                        const int m = lane + 64 * r;
+                        if (m < Sf) th[m] = (float)(((double)m + (double)uv[r]) / (double)Sf);
+                    }
+                } else {
+                    // i.i.d.: rank of each uniform (ties by index), then placed
+#pragma unroll
+                    for (int r = 0; r < RMAX; ++r)
+                        if (lane + 64 * r < Sf) th[lane + 64 * r] = uv[r];
+                    wave_sync_lds();
+                    // rank: the number of keys (bits of u_k, k) below (bits
+                    // of u_m, m) as unsigned 64-bit integers (nonnegative
+                    // floats order as their bits); 8 reads in flight
+                    int rank[RMAX];
+                    unsigned long long km[RMAX];
+#pragma unroll
+                    for (int r = 0; r < RMAX; ++r) {
+                        rank[r] = 0;
+                        km[r] = ((unsigned long long)__float_as_uint(uv[r]) << 32) | (unsigned)(lane + 64 * r);
+                    }
+                    for (int k0 = 0; k0 < Sf; k0 += 8) {
+                        float o[8];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) o[i] = th[min(k0 + i, Sf - 1)];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const unsigned long long ko = ((unsigned long long)__float_as_uint(o[i]) << 32) | (unsigned)(k0 + i);
+#pragma unroll
+                            for (int r = 0; r < RMAX; ++r) rank[r] += (int)((k0 + i < Sf) & (ko < km[r]));
+                        }
+                    }
+                    wave_sync_lds();
+#pragma unroll
+                    for (int r = 0; r < RMAX; ++r)
+                        if (lane + 64 * r < Sf) th[rank[r]] = uv[r];
+                }
+                wave_sync_lds();
+                if (sampler == kSamplerStrat) {
+                    // thresholds (m + u_m)/S_f lie in [m/S_f, (m+1)/S_f]:
+                    // every m <= k-2 is below F and every m >= k+2 is not,
+                    // with k = floor(F S_f) (a margin of 1/S_f, far above the
+                    // rounding), so three comparisons give the exact count
+#pragma unroll
+                    for (int qq = 0; qq < EPL; ++qq) {
+                        const int k = (int)fminf(fmaxf(floorf(F[qq] * (float)Sf), 0.f), (float)Sf);
+                        const float a0 = th[max(k - 1, 0)], a1 = th[min(k, Sf - 1)], a2 = th[min(k + 1, Sf - 1)];
+                        cc[qq] = max(k - 1, 0) + (int)(k >= 1 && a0 < F[qq]) + (int)(k < Sf && a1 < F[qq]) +
+                                 (int)(k + 1 < Sf && a2 < F[qq]);
+                    }
+                } else {
+                    count_below_f(th, Sf, F, cc);   // i.i.d., long list: sorted, searched in lockstep
+                }
+            }
 #pragma unroll
             for (int qq = 0; qq < EPL; ++qq) {
                 const int j = lane * EPL + qq;
