@@ -14,14 +14,13 @@
 //
 // Precision plan (why index parity with an fp64 oracle holds): scores are
 // accumulated unscaled (bf16 products are exact in fp32; fp32 inputs use
-// fp64), the tile max is subtracted before the scale is applied, the reducer
-// works in fp64, and the CDF positions of pass 2 are formed in fp64.
+// fp64), the tile max is subtracted before the scale is applied, and the
+// local CDF positions P_j / Z_t are fp32 with thresholds formed in fp64.
 #include "santa_kernels.h"
 
 namespace santa {
 
-// #{m in [0, len) : th[m] < F} for a nondecreasing fp32 list
-// c[i] = #{m < len : th[m] < F[i]} for a nondecreasing list, the N searches
+// c[i] = #{m < len : th[m] < F[i]} for a nondecreasing fp32 list, the N searches
 // in lockstep (binary lifting: c grows by each power of two, largest first,
 // while th[c + step - 1] < F), so that their LDS reads are in flight together
 template <int N>
@@ -51,9 +50,11 @@ __device__ __forceinline__ void count_below_f(const float *th, int len, const fl
 // local thresholds on the local CDF P_j / Z_t, and the same per-element count
 // rule as pass 2 of prop (counts of thresholds below each position, monotone,
 // forced to S_f from the last nonzero weight on).  Systematic thresholds
-// u_f + m/S_f (u_f = U * n_t) have closed-form counts; with LIST the S_f
-// thresholds of the tile, (m + u_m)/S_f or the tile's uniforms sorted, are
-// an LDS list searched by bisection.
+// u_f + m/S_f (u_f = U * n_t) have closed-form counts.  With LIST: the
+// stratified thresholds (m + u_m)/S_f go to an LDS list read by a
+// three-comparison closed form; i.i.d. counts of up to 64 uniforms are taken
+// across the wave from registers (the count does not depend on the order),
+// longer lists are sorted in LDS and searched in lockstep.
 template <typename KV, int G, int T, bool PAGED, bool LIST>
 __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
     const typename QOf<KV>::type *__restrict__ q, const KV *__restrict__ k, const KV *__restrict__ v, KVLayout L,
