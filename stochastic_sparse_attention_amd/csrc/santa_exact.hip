@@ -12,10 +12,10 @@
 // The exact split-KV decode is the FlashDecoding-style baseline the pages
 // compare against.
 //
-// Precision plan (why index parity with an fp64 oracle holds): scores are
-// accumulated unscaled (bf16 products are exact in fp32; fp32 inputs use
-// fp64), the tile max is subtracted before the scale is applied, the reducer
-// works in fp64, and the CDF positions of pass 2 are formed in fp64.
+// Precision: scores are accumulated unscaled as in prop (bf16 products are
+// exact in fp32; fp32 inputs use fp64), the tile max is subtracted before the
+// scale is applied, each tile's weights and weighted V sums are fp32, and
+// the merge of the tiles works in fp64.
 #include "santa_kernels.h"
 
 namespace santa {

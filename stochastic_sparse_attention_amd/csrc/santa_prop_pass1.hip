@@ -1,7 +1,7 @@
 // santa_prop_pass1.hip -- S2ANTA-prop, pass 1: scores, tile max, tile
 // partition function and the exponentiated-score stash (its own translation
-// unit; the reducer, pass 2 and the launcher of the step are in
-// santa_prop.hip).
+// unit; the reducer and pass 2 are in santa_prop.hip, and santa_dispatch.cpp
+// launches the step).
 //
 // The method follows the web page "Stochastic Sparse Attention for
 // Memory-Bound Inference" (ICML 2026 paper notes on SANTA), key design 2:
