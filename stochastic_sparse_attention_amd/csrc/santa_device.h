@@ -31,9 +31,9 @@ struct KVLayout {
 // (j0 % 16 == 0); rows j0..j0+15 are contiguous in both layouts.
 __device__ __forceinline__ size_t block16_offset(const KVLayout &L, int b, int g, int j0) {
     if (L.page_size == 0)
-        return ((size_t)(b * L.num_kv_heads + g) * L.max_seq_len + j0) * kHeadDim;
+        return (((size_t)b * L.num_kv_heads + g) * L.max_seq_len + j0) * kHeadDim;
     int page = L.page_table[(size_t)b * L.max_pages + j0 / L.page_size];
-    return ((size_t)(page * L.num_kv_heads + g) * L.page_size + (j0 % L.page_size)) * kHeadDim;
+    return (((size_t)page * L.num_kv_heads + g) * L.page_size + (j0 % L.page_size)) * kHeadDim;
 }
 
 __device__ __forceinline__ size_t row_offset(const KVLayout &L, int b, int g, int j) {

@@ -53,9 +53,9 @@ __device__ __forceinline__ size_t block_base(const KVLayout &L, int b, int g, in
     const int jb = j0 < n ? j0 : t0;
     if (PAGED) {
         const int page = L.page_table[(size_t)b * L.max_pages + jb / L.page_size];
-        return ((size_t)(page * L.num_kv_heads + g) * L.page_size + (jb % L.page_size)) * kHeadDim;
+        return (((size_t)page * L.num_kv_heads + g) * L.page_size + (jb % L.page_size)) * kHeadDim;
     }
-    return ((size_t)(b * L.num_kv_heads + g) * L.max_seq_len + jb) * kHeadDim;
+    return (((size_t)b * L.num_kv_heads + g) * L.max_seq_len + jb) * kHeadDim;
 }
 
 // ------------------------------------------------------------------ MFMA

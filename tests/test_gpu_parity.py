@@ -356,6 +356,63 @@ def test_full_size_prop(gpu, cid):
         _say("full flash cfg", cid, parity.check_flash(dev, cfg.S_flash, repeat=False))
 
 
+# ------------------------------------------------- offsets past 2^31 elements
+def test_kv_cache_past_2_pow_31_elements(gpu):
+    """A KV cache of more than 2^31 elements: 17 requests x 8 KV heads x
+    131072 tokens x 128 (4.6 GB each for K and V).  The last request sits at
+    the highest offsets; its heads must give bitwise the results of the same
+    request run alone (prop, flash and exact decode), which are themselves
+    held to the oracle bar."""
+    import torch
+    import parity
+    import stochastic_sparse_attention_amd as sa
+    cfg = synth.small_config(4, batch=1, seq_len=131072, num_q_heads=8, num_kv_heads=8)
+    dev = _dev(cfg, 31, gpu)
+    S, T, B = cfg.S, cfg.tile_len, 17
+    nt = cfg.seq_len // T
+    SF = 2 * nt
+    _say("single request vs oracle, prop", parity.check_prop(dev, S, repeat=False))
+    _say("single request vs oracle, flash", parity.check_flash(dev, SF, repeat=False))
+    out_s, idx_s, tb_s = parity.run_prop(dev, S)
+    outf_s, idxf_s = parity.run_flash(dev, SF)
+    oute_s = parity.run_exact(dev)
+
+    H, Hkv, n, d = cfg.num_q_heads, cfg.num_kv_heads, cfg.seq_len, cfg.head_dim
+    assert B * Hkv * n * d > 2 ** 31
+    g = torch.Generator(device=gpu)
+    g.manual_seed(5)
+    q = torch.randn((B, H, d), generator=g, device=gpu).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, n, d), generator=g, device=gpu, dtype=torch.bfloat16)
+    v = torch.randn((B, Hkv, n, d), generator=g, device=gpu, dtype=torch.bfloat16)
+    q[B - 1].copy_(dev.q.view(1, H, d)[0])
+    k[B - 1].copy_(dev.k.view(1, Hkv, n, d)[0])
+    v[B - 1].copy_(dev.v.view(1, Hkv, n, d)[0])
+    u = torch.rand(B * H, generator=g, device=gpu) / S
+    u[(B - 1) * H:] = dev.u(S)
+    uf = torch.rand(B * H, generator=g, device=gpu) / SF
+    uf[(B - 1) * H:] = dev.u(SF)
+    prob = sa.Problem(B, H, Hkv, d, n, dtype="bf16", scale=dev.inp.scale, tile_len=T)
+    out = torch.empty((B * H, d), dtype=torch.float32, device=gpu)
+    idx = torch.empty((B * H, S), dtype=torch.int32, device=gpu)
+    tb = torch.empty((B * H, nt), dtype=torch.int32, device=gpu)
+    sa.santa_decode_prop(prob, q, k, v, S, u, out, idx, tb)
+    torch.cuda.synchronize()
+    last = slice((B - 1) * H, B * H)
+    assert np.array_equal(out[last].cpu().numpy().view(np.uint32), out_s.view(np.uint32))
+    assert np.array_equal(idx[last].cpu().numpy(), idx_s) and np.array_equal(tb[last].cpu().numpy(), tb_s)
+    outf = torch.empty_like(out)
+    idxf = torch.empty((B * H, SF), dtype=torch.int32, device=gpu)
+    sa.santa_decode_flash(prob, q, k, v, SF, uf, outf, idxf)
+    torch.cuda.synchronize()
+    assert np.array_equal(outf[last].cpu().numpy().view(np.uint32), outf_s.view(np.uint32))
+    assert np.array_equal(idxf[last].cpu().numpy(), idxf_s)
+    oute = torch.empty_like(out)
+    sa.exact_decode_ref(prob, q, k, v, oute)
+    torch.cuda.synchronize()
+    assert np.array_equal(oute[last].cpu().numpy().view(np.uint32), oute_s.view(np.uint32))
+    _say("offsets past 2^31 elements: last request bitwise equal (prop, flash, exact)")
+
+
 # ------------------------------------------------- HIP graph replay
 def test_graph_replays_match_eager(gpu):
     """prop (all three threshold generators), flash (systematic and
