@@ -64,11 +64,8 @@ __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
     typedef typename ScorerFor<KV, G, T, PAGED>::type SC;
     typedef typename SC::acc_t acc_t;
     constexpr int EPL = T / 64;
-    // tile-fastest numbering: consecutive blocks stream consecutive tiles of
-    // one KV head (adjacent 64 KiB pieces of K for T = 256)
-    const int tile = blockIdx.x % nt;
-    const int bg = blockIdx.x / nt;
-    const int b = bg / L.num_kv_heads, g = bg - b * L.num_kv_heads;
+    int tile, b, g;
+    tile_of_block<PAGED>(L, nt, tile, b, g);
     const int n = L.max_seq_len;
     const int t0 = tile * T;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;

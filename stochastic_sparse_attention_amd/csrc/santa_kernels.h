@@ -112,6 +112,28 @@ __device__ __forceinline__ V block_shift_up(V v, V first, V *sh) {
 }
 
 // exp-weight e = exp(scale (x - m)) of an unscaled score x, tile max m
+// (tile, request, KV head) of this workgroup in the per-tile kernels.
+// Contiguous K: tile fastest, so consecutive blocks stream adjacent pieces of
+// one KV head (64 KiB each for T = 256).  Paged K ([pages, Hkv, 16, d]): KV
+// head fastest, so consecutive blocks read the heads' adjacent 4 KiB pieces
+// of the same pages; tile-fastest order would have them all read one head's
+// pieces at the Hkv * 4 KiB page stride (16% slower on pages held in order).
+template <bool PAGED>
+__device__ __forceinline__ void tile_of_block(const KVLayout &L, int max_nt, int &tile, int &b, int &g) {
+    const int id = blockIdx.x;
+    if (PAGED) {
+        g = id % L.num_kv_heads;
+        const int rest = id / L.num_kv_heads;
+        tile = rest % max_nt;
+        b = rest / max_nt;
+    } else {
+        tile = id % max_nt;
+        const int bg = id / max_nt;
+        b = bg / L.num_kv_heads;
+        g = bg - b * L.num_kv_heads;
+    }
+}
+
 template <typename acc_t>
 __device__ __forceinline__ float exp_weight(acc_t x, float m, acc_t c2) {
     return exp2f((float)((x - (acc_t)m) * c2));

@@ -407,8 +407,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(LIST
     __shared__ int wrow[NW][kWave];        // per-wave compacted marker rows
     __shared__ float wmul[NW][kWave];      // and their multiplicities
 
-    // block -> (request, KV head, head in group); blocks of one KV head are
-    // numbered bg + i * B*Hkv, the numbering pass 1 uses for that head's tiles
+    // block -> (request, KV head, head in group): block bg + i * B*Hkv takes
+    // head i of the group of (request, KV head) bg
     const int BG = batch * L.num_kv_heads;
     const int bg = blockIdx.x % BG, hl = blockIdx.x / BG;
     const int b = bg / L.num_kv_heads, g = bg - b * L.num_kv_heads;

@@ -24,11 +24,8 @@ __global__ __launch_bounds__(kBlock) void prop_pass1_kernel(
     int num_q_heads, int max_nt, float scale, float *__restrict__ stash, float2 *__restrict__ stats) {
     typedef typename ScorerFor<KV, G, T, PAGED>::type SC;
     typedef typename SC::acc_t acc_t;
-    // tile-fastest numbering: consecutive blocks stream consecutive tiles of
-    // one KV head (adjacent 64 KiB pieces of K for T = 256)
-    const int tile = blockIdx.x % max_nt;
-    const int bg = blockIdx.x / max_nt;
-    const int b = bg / L.num_kv_heads, g = bg - b * L.num_kv_heads;
+    int tile, b, g;
+    tile_of_block<PAGED>(L, max_nt, tile, b, g);
     const int n = seq_len_of(seq_lens, L.max_seq_len, b);
     const int t0 = tile * T;
     if (t0 >= n) return;
