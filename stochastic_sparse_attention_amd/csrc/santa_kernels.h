@@ -14,8 +14,10 @@ namespace santa {
 #ifndef SANTA_SAMPLE_MANY_HEADS
 #define SANTA_SAMPLE_MANY_HEADS 512
 #endif
-// above this many heads the systematic sampling kernel runs 8 waves per head
+// above this many heads the systematic sampling kernel runs 8 waves per head,
+// above kSampleVeryManyHeads 4 (every head of a batch of 64 resident at once)
 constexpr int kSampleManyHeads = SANTA_SAMPLE_MANY_HEADS;
+constexpr int kSampleVeryManyHeads = 1024;
 // the same for the list generators, whose 16-wave workgroups take a whole
 // compute unit each (more registers)
 constexpr int kSampleListManyHeads = 256;

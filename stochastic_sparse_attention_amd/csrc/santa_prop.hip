@@ -373,7 +373,7 @@ __device__ __forceinline__ float float_at_or_below(double x) {
 
 // LIST: stratified / i.i.d. thresholds (a sorted list in LDS); else the
 // systematic closed form
-// NW: waves per workgroup (16, or 8 for many heads: more heads per CU)
+// NW: waves per workgroup (16; 8 or 4 for many heads: more heads per CU)
 // Registers: systematic, at most 64 VGPRs (8 waves per SIMD), so that two
 // 16-wave or four 8-wave workgroups share a compute unit; list generators,
 // at most 128 (4 waves per SIMD): one 16-wave or two 8-wave workgroups.
@@ -748,6 +748,7 @@ static hipError_t launch_sample_t(const LaunchArgs &a, const TimingHook &) {
     if (a.sampler != kSamplerSys)
         return many ? launch(prop_sample_kernel<KV, T, PAGED, true, 8>, 8)
                     : launch(prop_sample_kernel<KV, T, PAGED, true, 16>, 16);
+    if (BH > kSampleVeryManyHeads) return launch(prop_sample_kernel<KV, T, PAGED, false, 4>, 4);
     if (many) return launch(prop_sample_kernel<KV, T, PAGED, false, 8>, 8);
     return launch(prop_sample_kernel<KV, T, PAGED, false, 16>, 16);
 }

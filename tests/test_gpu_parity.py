@@ -145,14 +145,17 @@ def test_sampler_variance_ordering(gpu):
     assert mse["sys"] < mse["iid"] and mse["strat"] < mse["iid"]
 
 
-def test_prop_many_heads(gpu):
+@pytest.mark.parametrize("batch", [24, 40])
+def test_prop_many_heads(gpu, batch):
     """More than 512 heads: the systematic sampling kernel runs 8 waves per
-    head.  Mixed lengths (some short requests), paged KV and S = 1000."""
+    head (768 heads), and 4 above 1024 (1280 heads).  Mixed lengths (some
+    short requests), paged KV, S = 128 and S = 1000."""
     import parity
-    cfg = synth.small_config(5, batch=24, seq_len=2500, min_seq_len=64)
+    cfg = synth.small_config(5, batch=batch, seq_len=2500, min_seq_len=64)
     dev = _dev(cfg, 19, gpu)
-    _say("768 heads, S=128", parity.check_prop(dev, 128))
-    _say("768 heads, S=1000", parity.check_prop(dev, 1000, repeat=False))
+    BH = batch * cfg.num_q_heads
+    _say(BH, "heads, S=128", parity.check_prop(dev, 128))
+    _say(BH, "heads, S=1000", parity.check_prop(dev, 1000, repeat=False))
 
 
 @pytest.mark.parametrize("sampler", ["strat", "iid"])
