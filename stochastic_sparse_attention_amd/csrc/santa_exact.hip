@@ -38,12 +38,13 @@ __global__ __launch_bounds__(kBlock) void exact_partial_kernel(
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 
     // LDS: the scorer's staging area, then (after the barrier in tile_max)
-    // the tile's weights Pw[G][T] and the per-wave V sums red_o
+    // the tile's weights Pw[T][G] (a row's G weights in one LDS read) and the
+    // per-wave V sums red_o
     constexpr int kPwBytes = G * T * 4, kRedBytes = kWavesPerBlock * G * kHeadDim * 4;
     __shared__ __align__(16) unsigned char lds[cmax(SC::kStageVec * 16, kPwBytes + kRedBytes)];
     __shared__ float red_m[kWavesPerBlock][16];
     __shared__ float red_l[kWavesPerBlock][16];
-    float (*Pw)[T] = reinterpret_cast<float (*)[T]>(lds);
+    float *Pw = reinterpret_cast<float *>(lds);   // [T][G]
     float (*red_o)[G][kHeadDim] = reinterpret_cast<float (*)[G][kHeadDim]>(lds + kPwBytes);
 
     SC sc;
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(kBlock) void exact_partial_kernel(
             for (int s = 0; s < SC::NS; ++s) {
                 const int row = SC::row(lane, w, s);
                 const float p = (t0 + row < n) ? exp_weight(sc.x[s][v], mt[v], c2) : 0.f;
-                Pw[hl][row] = p;
+                Pw[row * G + hl] = p;
                 lsum += p;
             }
         }
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(kBlock) void exact_partial_kernel(
                 widen8(vv[ii][r4], xv);
 #pragma unroll
                 for (int hl = 0; hl < G; ++hl) {
-                    const float p = Pw[hl][row];
+                    const float p = Pw[row * G + hl];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) acc[hl][e] = fmaf(p, xv[e], acc[hl][e]);
                 }
