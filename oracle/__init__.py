@@ -21,6 +21,10 @@ Functions and their pins (the tests under tests/ hold the checks):
   iid / strat thresholds              i.i.d. variance closed form
   replay                              equals the estimate for the oracle's own
                                       indices
+  bernoulli_* / santa_prop_bernoulli  E[score] = <q, K> exactly over a grid of
+                                      uniforms; hand-derived coefficients;
+                                      |q_i| = max|q| reduces to exact scores
+                                      (and prop); read fraction closed form
 """
 from __future__ import annotations
 
@@ -77,6 +81,11 @@ def lib():
         L.oracle_estimate_from_weights.argtypes = [dp, C.c_int, dp, C.c_int, dp, C.c_int, dp]
         L.oracle_sys_moments.argtypes = [dp, C.c_int, dp, C.c_int, C.c_int, dp, dp]
         L.oracle_flash_moments.argtypes = [dp, C.c_int, dp, C.c_int, C.c_int, C.c_int, dp, dp]
+        L.oracle_bernoulli_coefs.argtypes = [fp, C.c_int, fp, C.c_int, ip, fp]
+        L.oracle_bernoulli_logits.argtypes = [P, vp, vp, C.c_int, C.c_int, fp, C.c_int, C.c_int, dp]
+        L.oracle_bernoulli_features.argtypes = [P, vp, C.c_int, C.c_int, fp, ip]
+        L.oracle_santa_prop_bernoulli.argtypes = [P, vp, vp, vp, C.c_int, fp, C.c_int, C.c_int, fp,
+                                                  dp, ip, dp, ip]
         L.oracle_num_threads.restype = C.c_int
         L.oracle_set_num_threads.argtypes = [C.c_int]
         _lib = L
@@ -312,6 +321,63 @@ def replay(prob: Problem, v, S, idx, ptile=None):
     if rc:
         raise ValueError(f"oracle_replay: {rc}")
     return out
+
+
+def _fptr(a):
+    return a.ctypes.data_as(C.POINTER(C.c_float))
+
+
+def bernoulli_coefs(qf, u, draws):
+    """Ternary coefficients c [d] (sum of `draws` draws), the scale a and the
+    number of nonzero c for one fp32 query qf [d] and uniforms u [draws, d]."""
+    qf = np.ascontiguousarray(qf, np.float32)
+    u = np.ascontiguousarray(u, np.float32).reshape(draws, qf.size)
+    c = np.empty(qf.size, np.int32)
+    a = C.c_float()
+    nz = lib().oracle_bernoulli_coefs(_fptr(qf), qf.size, _fptr(u), draws, _iptr(c), C.byref(a))
+    if nz < 0:
+        raise ValueError("oracle_bernoulli_coefs: uniform outside [0, 1)")
+    return c, a.value, nz
+
+
+def bernoulli_logits(prob: Problem, q, k, draws, group_mean, ub, b, h):
+    """Bernoulli-estimated scores of head h of request b (fp64)."""
+    n = prob.max_seq_len if prob.seq_lens is None else int(prob.seq_lens[b])
+    x = np.empty(n, np.float64)
+    ub = np.ascontiguousarray(ub, np.float32)
+    nz = lib().oracle_bernoulli_logits(prob.ref, _vp(q), _vp(k), draws, int(group_mean), _fptr(ub),
+                                       b, h, _dptr(x))
+    if nz < 0:
+        raise ValueError("oracle_bernoulli_logits: uniform outside [0, 1)")
+    return x, nz
+
+
+def bernoulli_features(prob: Problem, q, draws, group_mean, ub):
+    """Features read per KV group [B*Hkv]: the union over its heads."""
+    nread = np.empty(prob.batch * prob.s.num_kv_heads, np.int32)
+    ub = np.ascontiguousarray(ub, np.float32)
+    rc = lib().oracle_bernoulli_features(prob.ref, _vp(q), draws, int(group_mean), _fptr(ub),
+                                         _iptr(nread))
+    if rc:
+        raise ValueError(f"oracle_bernoulli_features: {rc}")
+    return nread
+
+
+def santa_prop_bernoulli(prob: Problem, q, k, v, S, u, draws, group_mean, ub):
+    """S2ANTA-prop (systematic) on Bernoulli qK^T scores."""
+    BH, d = prob.batch * prob.num_q_heads, prob.head_dim
+    u = np.ascontiguousarray(u, np.float32)
+    ub = np.ascontiguousarray(ub, np.float32)
+    out = np.empty((BH, d), np.float64)
+    idx = np.empty((BH, S), np.int32)
+    dl = np.empty((BH, S), np.float64)
+    tc = np.empty((BH, prob.max_tiles()), np.int32)
+    rc = lib().oracle_santa_prop_bernoulli(prob.ref, _vp(q), _vp(k), _vp(v), S, _fptr(u), draws,
+                                           int(group_mean), _fptr(ub), _dptr(out), _iptr(idx),
+                                           _dptr(dl), _iptr(tc))
+    if rc:
+        raise ValueError(f"oracle_santa_prop_bernoulli: {rc}")
+    return {"out": out, "idx": idx, "delta": dl, "tile_counts": tc}
 
 
 def num_threads():

@@ -18,6 +18,10 @@
  *                        reducer, per-tile budgets proportional to tile mass
  *   [key design 3]       S2ANTA-flash: S/(number of tiles) local samples per
  *                        tile, rescaled by the true tile mass at merge time
+ *   [key design 4]       Bernoulli qK^T: the query scaled into [-1, 1], its
+ *                        magnitudes taken as Bernoulli probabilities, ternary
+ *                        queries, an unbiased score estimate, sparse feature
+ *                        reads of K; [ablations] the mean group query for GQA
  *
  * Readings taken where the page is silent (each is listed in the design
  * notes as well):
@@ -33,7 +37,14 @@
  *   R6  flash uses one offset per head, scaled to the per-tile budget:
  *       u_f = U * n_t in [0, 1/S_f), S_f = S / n_t;
  *   R10 GQA maps q head h to KV head h / (Hq / Hkv);
- *   R11 a request with zero keys is empty: output 0, indices -1, budgets 0.
+ *   R11 a request with zero keys is empty: output 0, indices -1, budgets 0;
+ *   R15 Bernoulli qK^T: "B" is the number of independent ternary draws that
+ *       are averaged; the scale into [-1, 1] is a = max_i |q_i|; draw r takes
+ *       z_i = sign(q_i) when fl32(u_{r,i} * a) < |q_i|, else 0 (the decision
+ *       is taken in fp32, as the GPU takes it);
+ *   R16 the mean group query is the fp32 mean of the group's G queries, summed
+ *       in head order and multiplied by 1/G; all G heads then share its
+ *       ternary draws and therefore its scores.
  *
  * All arithmetic is IEEE double.  Inputs (bf16 or fp32) are widened exactly.
  */
@@ -126,6 +137,136 @@ void oracle_logits(const oracle_problem *p, const void *q, const void *k,
             dot += load_val(q, qoff + i, p->q_fmt) * load_val(k, koff + i, p->kv_fmt);
         x[j] = (double)p->scale * dot;
     }
+}
+
+static int lengths_ok(const oracle_problem *p);
+
+/* ------------------------------------------------------------------ */
+/* O13 -- Bernoulli qK^T [key design 4].  a = max_i |q_i| scales the    */
+/* query into [-1, 1]; |q_i| / a is the probability that a ternary draw */
+/* keeps feature i, with the sign of q_i (R15).  Summing `draws` draws  */
+/* gives integer coefficients c_i in [-draws, draws]; the score         */
+/* estimate is (a / draws) * sum_i c_i K_{j,i}, unbiased since          */
+/* E[c_i] = draws * q_i / a.  Only features with c_i != 0 are read.     */
+/*   qf [d] the query in fp32; u [draws, d] uniforms in [0,1).           */
+/* Writes c[d] and *a_out; returns the number of features with c != 0,  */
+/* or -1 if a uniform lies outside [0,1).                               */
+/* ------------------------------------------------------------------ */
+int oracle_bernoulli_coefs(const float *qf, int d, const float *u, int draws, int *c, float *a_out)
+{
+    float a = 0.0f;
+    for (int i = 0; i < d; ++i) {
+        float m = fabsf(qf[i]);
+        if (m > a) a = m;
+    }
+    int nz = 0, bad = 0;
+    for (int i = 0; i < d; ++i) {
+        float mag = fabsf(qf[i]);
+        int sgn = qf[i] > 0.0f ? 1 : (qf[i] < 0.0f ? -1 : 0);
+        int kept = 0;
+        for (int r = 0; r < draws; ++r) {
+            float ur = u[(size_t)r * d + i];
+            if (!(ur >= 0.0f && ur < 1.0f)) bad = 1;
+            float prod = ur * a;                 /* one fp32 rounding */
+            if (prod < mag) kept += 1;
+        }
+        c[i] = sgn * kept;
+        if (c[i] != 0) nz += 1;
+    }
+    *a_out = a;
+    return bad ? -1 : nz;
+}
+
+/* The query that head h's Bernoulli draws are taken from (fp32): its own
+   (exact widening), or with the mean group query (R16) the fp32 mean of the
+   group's G queries, summed in head order. */
+static void bernoulli_query(const oracle_problem *p, const void *q, int group_mean, int b, int h,
+                            float *qf)
+{
+    int d = p->head_dim, G = p->num_q_heads / p->num_kv_heads;
+    if (!group_mean) {
+        size_t off = ((size_t)b * p->num_q_heads + h) * d;
+        for (int i = 0; i < d; ++i) qf[i] = (float)load_val(q, off + i, p->q_fmt);
+        return;
+    }
+    int h0 = kv_head_of(p, h) * G;
+    for (int i = 0; i < d; ++i) {
+        float s = (float)load_val(q, ((size_t)b * p->num_q_heads + h0) * d + i, p->q_fmt);
+        for (int hh = 1; hh < G; ++hh)
+            s = s + (float)load_val(q, ((size_t)b * p->num_q_heads + h0 + hh) * d + i, p->q_fmt);
+        qf[i] = s * (1.0f / (float)G);
+    }
+}
+
+/* Uniforms of head h: [B, Hq, draws, d] per head, or [B, Hkv, draws, d]
+   with the mean group query (one set per group). */
+static const float *bernoulli_uniforms(const oracle_problem *p, const float *ub, int draws,
+                                       int group_mean, int b, int h)
+{
+    int d = p->head_dim;
+    size_t owner = group_mean ? (size_t)b * p->num_kv_heads + kv_head_of(p, h)
+                              : (size_t)b * p->num_q_heads + h;
+    return ub + owner * (size_t)draws * d;
+}
+
+/* Estimated scores of head h of request b:
+     x_j = scale * (a / draws) * sum_i c_i K_{j,i}     (fp64 sum)
+   Returns the number of features head h reads, or -1 on a bad uniform. */
+int oracle_bernoulli_logits(const oracle_problem *p, const void *q, const void *k, int draws,
+                            int group_mean, const float *ub, int b, int h, double *x)
+{
+    int d = p->head_dim, g = kv_head_of(p, h), n = seq_len_of(p, b);
+    float *qf = (float *)malloc(sizeof(float) * (size_t)d);
+    int *c = (int *)malloc(sizeof(int) * (size_t)d);
+    float a = 0.0f;
+    bernoulli_query(p, q, group_mean, b, h, qf);
+    int nz = oracle_bernoulli_coefs(qf, d, bernoulli_uniforms(p, ub, draws, group_mean, b, h),
+                                    draws, c, &a);
+    double coef = (double)p->scale * ((double)a / (double)draws);
+    for (int j = 0; j < n; ++j) {
+        size_t koff = kv_row_offset(p, b, g, j);
+        double dot = 0.0;
+        for (int i = 0; i < d; ++i)
+            if (c[i] != 0) dot += (double)c[i] * load_val(k, koff + i, p->kv_fmt);
+        x[j] = coef * dot;
+    }
+    free(qf);
+    free(c);
+    return nz;
+}
+
+/* Features of K that KV group (b, g) reads: the union over the group's
+   heads of { i : c_i != 0 } (one query with the mean group query).
+   nread [B*Hkv].  Returns 0, or -1 on bad arguments or uniforms. */
+int oracle_bernoulli_features(const oracle_problem *p, const void *q, int draws, int group_mean,
+                              const float *ub, int *nread)
+{
+    if (draws < 1 || !lengths_ok(p)) return -1;
+    int d = p->head_dim, G = p->num_q_heads / p->num_kv_heads, status = 0;
+    float *qf = (float *)malloc(sizeof(float) * (size_t)d);
+    int *c = (int *)malloc(sizeof(int) * (size_t)d);
+    char *any = (char *)malloc((size_t)d);
+    for (int b = 0; b < p->batch; ++b)
+        for (int g = 0; g < p->num_kv_heads; ++g) {
+            memset(any, 0, (size_t)d);
+            for (int hl = 0; hl < (group_mean ? 1 : G); ++hl) {
+                int h = g * G + hl;
+                float a;
+                bernoulli_query(p, q, group_mean, b, h, qf);
+                if (oracle_bernoulli_coefs(qf, d, bernoulli_uniforms(p, ub, draws, group_mean, b, h),
+                                           draws, c, &a) < 0)
+                    status = -3;
+                for (int i = 0; i < d; ++i)
+                    if (c[i] != 0) any[i] = 1;
+            }
+            int cnt = 0;
+            for (int i = 0; i < d; ++i) cnt += any[i];
+            nread[(size_t)b * p->num_kv_heads + g] = cnt;
+        }
+    free(qf);
+    free(c);
+    free(any);
+    return status;
 }
 
 /* ------------------------------------------------------------------ */
@@ -279,11 +420,17 @@ static int max_tiles(const oracle_problem *p)
 /*   tile_cnt [B*Hq*max_nt] thresholds per tile, S_t (NULL allowed)    */
 /* Returns 0, or a negative code on bad arguments.                      */
 /* ------------------------------------------------------------------ */
-int oracle_santa_prop_sampler(const oracle_problem *p, const void *q, const void *k,
-                              const void *v, int S, int kind, const float *u, double *out,
-                              int *idx, double *delta, int *tile_cnt)
+typedef struct {
+    int draws, group_mean;
+    const float *ub;
+} bernoulli_args;
+
+static int prop_core(const oracle_problem *p, const void *q, const void *k, const void *v,
+                     int S, int kind, const float *u, const bernoulli_args *bern, double *out,
+                     int *idx, double *delta, int *tile_cnt)
 {
     if (S <= 0 || kind < 0 || kind > 2 || !lengths_ok(p)) return -1;
+    if (bern && bern->draws < 1) return -1;
     int H = p->num_q_heads, d = p->head_dim, mnt = max_tiles(p);
     int status = 0;
     int nheads = p->batch * H;
@@ -306,7 +453,14 @@ int oracle_santa_prop_sampler(const oracle_problem *p, const void *q, const void
         double *u01 = (double *)malloc(sizeof(double) * (size_t)S);
         int *J = (int *)malloc(sizeof(int) * (size_t)S);
         double *dl = (double *)malloc(sizeof(double) * (size_t)S);
-        oracle_logits(p, q, k, b, h, x);
+        if (bern) {
+            if (oracle_bernoulli_logits(p, q, k, bern->draws, bern->group_mean, bern->ub, b, h, x) < 0) {
+#pragma omp atomic write
+                status = -3;
+            }
+        } else {
+            oracle_logits(p, q, k, b, h, x);
+        }
         oracle_softmax_weights(x, n, e, NULL);
         if (kind == 0) {
             double U = (double)u[bh];
@@ -346,12 +500,31 @@ int oracle_santa_prop_sampler(const oracle_problem *p, const void *q, const void
     return status;
 }
 
+int oracle_santa_prop_sampler(const oracle_problem *p, const void *q, const void *k,
+                              const void *v, int S, int kind, const float *u, double *out,
+                              int *idx, double *delta, int *tile_cnt)
+{
+    return prop_core(p, q, k, v, S, kind, u, NULL, out, idx, delta, tile_cnt);
+}
+
 /* S2ANTA-sys prop: the systematic generator of the function above. */
 int oracle_santa_prop(const oracle_problem *p, const void *q, const void *k,
                       const void *v, int S, const float *u, double *out,
                       int *idx, double *delta, int *tile_cnt)
 {
-    return oracle_santa_prop_sampler(p, q, k, v, S, 0, u, out, idx, delta, tile_cnt);
+    return prop_core(p, q, k, v, S, 0, u, NULL, out, idx, delta, tile_cnt);
+}
+
+/* S2ANTA-prop (systematic thresholds) on Bernoulli qK^T scores (O13 in
+   place of O1; key design 4 composed with key design 2).  ub as for
+   oracle_bernoulli_logits; other arguments as for oracle_santa_prop. */
+int oracle_santa_prop_bernoulli(const oracle_problem *p, const void *q, const void *k,
+                                const void *v, int S, const float *u, int draws, int group_mean,
+                                const float *ub, double *out, int *idx, double *delta,
+                                int *tile_cnt)
+{
+    bernoulli_args ba = {draws, group_mean, ub};
+    return prop_core(p, q, k, v, S, 0, u, &ba, out, idx, delta, tile_cnt);
 }
 
 /* ------------------------------------------------------------------ */

@@ -189,6 +189,16 @@ class Inputs:
         n = self.cfg.batch * self.cfg.num_q_heads
         return (np.floor(rng.random((n, S)) * 2.0 ** 24) * 2.0 ** -24).astype(np.float32)
 
+    def bernoulli_uniforms(self, draws: int, group_mean: bool) -> np.ndarray:
+        """Uniforms in [0, 1) on the 2^-24 grid (exact in fp32) for the
+        ternary query draws of Bernoulli scoring: [B*Hq, draws, d] (one set
+        per head), or [B*Hkv, draws, d] when a group shares its mean query.
+        Their own stream, seeded by (seed, draws, group_mean)."""
+        c = self.cfg
+        rng = np.random.default_rng([self.seed, 0xBE7, draws, int(group_mean)])
+        owners = c.batch * (c.num_kv_heads if group_mean else c.num_q_heads)
+        return (np.floor(rng.random((owners, draws, c.head_dim)) * 2.0 ** 24) * 2.0 ** -24).astype(np.float32)
+
     @property
     def contiguous(self) -> bool:
         return self.cfg.page_size == 0

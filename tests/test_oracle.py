@@ -613,3 +613,152 @@ def test_oracle_e4m3_widening_through_logits():
     ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
     np.testing.assert_array_equal(np.isnan(x), np.isnan(ref))
     np.testing.assert_array_equal(x[~np.isnan(ref)], ref[~np.isnan(ref)])
+
+
+# ----------------------------------------------------- Bernoulli qK^T
+# Key design 4 of the SANTA notes: the query, scaled into [-1, 1], gives the
+# Bernoulli probabilities of a ternary query whose score estimate is unbiased.
+
+def _f32_problem(B, Hq, Hkv, d, n, T=64):
+    return O.Problem(B, Hq, Hkv, d, n, q_dtype="f32", kv_dtype="f32", scale=1.0, tile_len=T)
+
+
+def test_bernoulli_hand_derived_coefficients():
+    """q = [1, -0.5, 0.25, 0] (a = 1), two draws; uniforms laid out [draw, d].
+    Feature 0 (p = 1) is kept by both draws, feature 1 (p = 0.5) only by draw
+    0 (0.4 < 0.5, 0.6 > 0.5), feature 2 (p = 0.25) only by draw 1 (0.3, 0.2),
+    feature 3 (p = 0) never: c = [2, -1, 1, 0].  A [d, draw] reading of the
+    same array would give c_1 = -2."""
+    q = np.array([1, -0.5, 0.25, 0], np.float32)
+    u = np.array([[0.9, 0.4, 0.3, 0.0], [0.1, 0.6, 0.2, 0.5]], np.float32)
+    c, a, nz = O.bernoulli_coefs(q, u, 2)
+    assert c.tolist() == [2, -1, 1, 0] and a == 1.0 and nz == 3
+    # through the scores: x_j = (a / 2) * (2 K0 - K1 + K2), scale 1
+    k = np.array([[[[1.0, 2.0, 4.0, 8.0], [-3.0, 0.5, 0.25, 100.0]]]], np.float32)
+    prob = _f32_problem(1, 1, 1, 4, 2)
+    x, nz = O.bernoulli_logits(prob, q.reshape(1, 1, 4), k, 2, False, u.reshape(1, 2, 4), 0, 0)
+    assert nz == 3
+    assert x.tolist() == [0.5 * (2 * 1.0 - 2.0 + 4.0), 0.5 * (2 * -3.0 - 0.5 + 0.25)]
+
+
+def test_bernoulli_decision_is_strict_and_in_fp32():
+    """z is kept iff fl32(u * a) < |q_i|, strictly.  With a = 3 and |q| = 1:
+    u = fl32(1/3) gives u * 3 = 1.0 after fp32 rounding, not below 1, so the
+    feature is dropped; one fp32 step below, u * 3 rounds under 1 and it is
+    kept.  A product exactly equal to |q| (u = 0.5, a = 2) drops it too."""
+    q = np.array([3.0, 1.0], np.float32)
+    u13 = np.float32(1.0 / 3.0)
+    below = np.nextafter(u13, np.float32(0))
+    assert np.float32(u13 * np.float32(3)) == 1.0
+    assert np.float32(below * np.float32(3)) < 1.0
+    c, _, _ = O.bernoulli_coefs(q, np.array([[0.0, u13]], np.float32), 1)
+    assert c.tolist() == [1, 0]
+    c, _, _ = O.bernoulli_coefs(q, np.array([[0.0, below]], np.float32), 1)
+    assert c.tolist() == [1, 1]
+    c, _, _ = O.bernoulli_coefs(np.array([2.0, -1.0], np.float32), np.array([[0.5, 0.5]], np.float32), 1)
+    assert c.tolist() == [1, 0]          # u * a = 1.0 is not below |q| = 1
+    with pytest.raises(ValueError):
+        O.bernoulli_coefs(q, np.array([[0.0, 1.0]], np.float32), 1)
+
+
+@pytest.mark.parametrize("draws", [1, 3])
+def test_bernoulli_unbiased_on_exact_grid(draws):
+    """E[score] = scale <q, K> (key design 4).  Every |q_i| is a multiple
+    a k_i / N of a = 2 with N = 64, and each draw's uniform for feature i
+    runs over the N midpoints (m + 1/2)/N once as the run index m goes
+    round (shifted per draw and feature).  Exactly k_i of the N midpoints
+    fall below k_i / N, so the average over the N runs of each coefficient
+    is draws * q_i / a and the average score is the exact one, up to fp64
+    rounding."""
+    N, d, n, a = 64, 16, 5, 2.0
+    rng = np.random.default_rng(3)
+    kint = rng.integers(0, N + 1, size=d)
+    kint[0] = N                                  # the max, so a = 2
+    q = (a * kint / N * rng.choice([-1.0, 1.0], size=d)).astype(np.float32)
+    k = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+    prob = O.Problem(1, 1, 1, d, n, q_dtype="f32", kv_dtype="f32", scale=0.375, tile_len=64)
+    acc = np.zeros(n)
+    for m in range(N):
+        u = np.empty((draws, d), np.float32)
+        for r in range(draws):
+            for i in range(d):
+                u[r, i] = ((m + 7 * r + 3 * i) % N + 0.5) / N
+        x, _ = O.bernoulli_logits(prob, q.reshape(1, 1, d), k, draws, False, u.reshape(1, draws, d), 0, 0)
+        acc += x
+    want = 0.375 * (k[0, 0].astype(np.float64) @ q.astype(np.float64))
+    np.testing.assert_allclose(acc / N, want, rtol=0, atol=1e-12)
+
+
+def test_bernoulli_full_magnitude_query_is_exact():
+    """Every |q_i| equal to a: each draw keeps every feature with its sign,
+    c_i = draws * sign(q_i), and the estimate is the exact score for any
+    uniforms; prop on these scores selects what prop on exact scores does."""
+    cfg = synth.small_config(2, batch=2, seq_len=700, num_q_heads=4, num_kv_heads=2)
+    inp = synth.make_inputs(cfg, 11)
+    qv = synth.bf16_bits_to_f32(inp.q)
+    inp.q = synth.f32_to_bf16_bits(np.where(qv >= 0, 0.5, -0.5).astype(np.float32))
+    prob = O.Problem.from_inputs(inp)
+    for draws in (1, 4):
+        ub = inp.bernoulli_uniforms(draws, False)
+        for b, h in [(0, 0), (1, 3)]:
+            x, nz = O.bernoulli_logits(prob, inp.q, inp.k, draws, False, ub, b, h)
+            assert nz == cfg.head_dim
+            np.testing.assert_allclose(x, O.logits(prob, inp.q, inp.k, b, h), rtol=1e-13, atol=1e-13)
+        S = cfg.S
+        rb = O.santa_prop_bernoulli(prob, inp.q, inp.k, inp.v, S, inp.u(S), draws, False, ub)
+        re = O.santa_prop(prob, inp.q, inp.k, inp.v, S, inp.u(S))
+        assert np.array_equal(rb["idx"], re["idx"])
+        np.testing.assert_allclose(rb["out"], re["out"], rtol=0, atol=1e-12)
+        nread = O.bernoulli_features(prob, inp.q, draws, False, ub)
+        assert np.all(nread == cfg.head_dim)
+
+
+def test_bernoulli_zero_query_reads_nothing():
+    """q = 0: no feature is kept, every score is 0 and A is uniform."""
+    prob = _f32_problem(1, 2, 1, 8, 6)
+    q = np.zeros((1, 2, 8), np.float32)
+    k = np.random.default_rng(0).standard_normal((1, 1, 6, 8)).astype(np.float32)
+    ub = np.full((2, 2, 8), 0.25, np.float32)
+    x, nz = O.bernoulli_logits(prob, q, k, 2, False, ub, 0, 1)
+    assert nz == 0 and np.all(x == 0.0)
+    assert O.bernoulli_features(prob, q, 2, False, ub).tolist() == [0]
+
+
+def test_bernoulli_read_fraction_closed_form():
+    """P(feature i is read) = 1 - (1 - p_i)^draws for independent draws.  With
+    p_i = k_i / N and the two draws' uniforms enumerating all N^2 pairs of
+    midpoints, the count of runs that read feature i is N^2 - (N - k_i)^2
+    exactly; the sum over features is what the per-group counts add to."""
+    N, d = 8, 8
+    kint = np.array([8, 0, 1, 2, 3, 4, 5, 7])
+    q = (kint / N).astype(np.float32).reshape(1, 1, d)
+    prob = _f32_problem(1, 1, 1, d, 4)
+    mids = (np.arange(N) + 0.5) / N
+    total = 0
+    for u0 in mids:
+        for u1 in mids:
+            ub = np.stack([np.full(d, u0), np.full(d, u1)]).astype(np.float32).reshape(1, 2, d)
+            total += int(O.bernoulli_features(prob, q, 2, False, ub)[0])
+    assert total == int(np.sum(N * N - (N - kint) ** 2))
+
+
+def test_bernoulli_group_union_and_mean_query():
+    """Two heads in one KV group.  Without the mean group query the group
+    reads the union of the heads' kept features; with it, the fp32 mean
+    query [0.5, -1, 0.5, 0.25] (a = 1) is drawn once and both heads get its
+    scores."""
+    q = np.array([[[1.0, -1.0, 0.5, 0.0], [0.0, -1.0, 0.5, 0.5]]], np.float32)
+    k = np.array([[[[1.0, 2.0, 4.0, 8.0], [0.5, -1.0, 3.0, -2.0]]]], np.float32)
+    prob = _f32_problem(1, 2, 1, 4, 2)
+    # per head: head 0 keeps {0, 1}, head 1 keeps {1, 3}  -> union of 3
+    ub = np.array([[[0.5, 0.5, 0.75, 0.0]], [[0.5, 0.5, 0.75, 0.25]]], np.float32)
+    assert O.bernoulli_coefs(q[0, 0], ub[0], 1)[0].tolist() == [1, -1, 0, 0]
+    assert O.bernoulli_coefs(q[0, 1], ub[1], 1)[0].tolist() == [0, -1, 0, 1]
+    assert O.bernoulli_features(prob, q, 1, False, ub).tolist() == [3]
+    # mean query: p = [0.5, 1, 0.5, 0.25]; uniforms [0.25, 0.9, 0.5, 0.2]
+    ug = np.array([[[0.25, 0.9, 0.5, 0.2]]], np.float32)
+    assert O.bernoulli_coefs(np.array([0.5, -1, 0.5, 0.25], np.float32), ug[0], 1)[0].tolist() == [1, -1, 0, 1]
+    assert O.bernoulli_features(prob, q, 1, True, ug).tolist() == [3]
+    x0, _ = O.bernoulli_logits(prob, q, k, 1, True, ug, 0, 0)
+    x1, _ = O.bernoulli_logits(prob, q, k, 1, True, ug, 0, 1)
+    assert x0.tolist() == x1.tolist() == [1.0 - 2.0 + 8.0, 0.5 + 1.0 - 2.0]
