@@ -202,12 +202,52 @@ int exact_decode_ref(const santa_problem *p, const void *q, const void *k, const
                      float *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * S2ANTA-prop on Bernoulli qK^T scores ("key design 4", the score-stage
+ * sparsification, composed with "key design 2"; the mean group query is the
+ * one of the ablation table).  Pass 1 replaces the exact scores by an
+ * unbiased estimate from ternary queries: a query is scaled into [-1, 1] by
+ * a = max_i |q_i|, and each of `draws` independent draws keeps feature i,
+ * with the sign of q_i, when fl32(u * a) < |q_i| (u: that draw's uniform for
+ * feature i).  With c_i the sum of the draws, the score of key j is
+ * scale * (a / draws) * sum_i c_i K[j][i], whose expectation is the exact
+ * score.  Only features with c_i != 0 are read from K, which is therefore
+ * passed feature-major.  The reducer and pass 2 are those of
+ * santa_decode_prop (systematic thresholds).
+ *
+ * Built for (else SANTA_ERR_UNSUPPORTED): q_dtype = kv_dtype = SANTA_BF16,
+ * page_size = 0 (seq_lens may be given), max_seq_len % 4 == 0.
+ *   k_features   [B, Hkv, d, max_seq_len] bf16, 8-byte aligned (else
+ *                SANTA_ERR_INVALID): K transposed per KV head
+ *   v            [B, Hkv, max_seq_len, d] bf16 (the usual layout)
+ *   draws        ternary draws per query, 1..64 (else SANTA_ERR_INVALID)
+ *   group_mean   0: every q head draws its own ternary query, and its KV
+ *                group reads the union of their kept features.  1: the fp32
+ *                mean of the group's Hq/Hkv queries (summed in head order,
+ *                then multiplied by Hkv/Hq) is drawn once and every head of
+ *                the group takes its scores.  Other values: SANTA_ERR_INVALID
+ *   u_bern       fp32 uniforms in [0, 1): [B*Hq, draws, d] (group_mean 0) or
+ *                [B*Hkv, draws, d] (group_mean 1).  Not checked on the device:
+ *                the comparison above is applied to whatever is given
+ *   features_read [B*Hkv] int32 or NULL: the number of features of K the
+ *                group reads (kept by any of its draws), also for empty
+ *                requests
+ *   other arguments and the workspace (santa_workspace_size with
+ *   SANTA_VARIANT_PROP) as for santa_decode_prop
+ */
+int santa_decode_prop_bernoulli(const santa_problem *p, const void *q, const void *k_features,
+                                const void *v, int32_t S, const float *u, int32_t draws,
+                                int32_t group_mean, const float *u_bern, float *out,
+                                int32_t *sample_idx, int32_t *tile_budget, int32_t *features_read,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Optional timing hook for benchmarks.  When both events are non-NULL
  * (hipEvent_t), every later decode call made from the calling thread
  * records `begin` just before and `end` just after its dominant kernel (the
  * one that streams K: pass 1 for prop, the tile kernel for flash, the
- * partial kernel for exact) on the call's stream.  Pass NULL, NULL to turn
- * it off.  Thread-local; returns SANTA_OK.
+ * partial kernel for exact, the Bernoulli pass 1 for
+ * santa_decode_prop_bernoulli) on the call's stream.  Pass NULL, NULL to
+ * turn it off.  Thread-local; returns SANTA_OK.
  */
 int santa_set_timing_events(void *begin_event, void *end_event);
 

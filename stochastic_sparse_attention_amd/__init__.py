@@ -16,7 +16,7 @@ from ._lib import SantaError, santa_problem, SANTA_F32, SANTA_BF16, SANTA_FP8_E4
 
 __all__ = [
     "Problem", "santa_workspace_size", "santa_decode_prop", "santa_decode_prop_sampler", "santa_decode_flash",
-    "santa_decode_flash_sampler",
+    "santa_decode_flash_sampler", "santa_decode_prop_bernoulli",
     "exact_decode_ref", "santa_set_timing_events", "SantaError",
 ]
 
@@ -88,6 +88,21 @@ def santa_decode_prop_sampler(problem: Problem, q, k, v, S, sampler, u, out, sam
                                                _ptr(u), _ptr(out), _ptr(sample_idx), _ptr(tile_budget),
                                                _ptr(ws), ws.numel(), _stream(stream))
     _lib._check("santa_decode_prop_sampler", st)
+    return ws
+
+
+def santa_decode_prop_bernoulli(problem: Problem, q, k_features, v, S, u, draws, group_mean, u_bern, out,
+                                sample_idx=None, tile_budget=None, features_read=None, workspace=None,
+                                stream=None):
+    """prop on Bernoulli qK^T scores.  k_features: K transposed per KV head,
+    [B, Hkv, d, max_seq_len] bf16; u_bern: [B*Hq (or B*Hkv with group_mean),
+    draws, d] uniforms in [0, 1)."""
+    ws = _workspace(problem, "prop", S, workspace, q.device)
+    st = _lib.load().santa_decode_prop_bernoulli(problem.ref, _ptr(q), _ptr(k_features), _ptr(v), S, _ptr(u),
+                                                 int(draws), int(group_mean), _ptr(u_bern), _ptr(out),
+                                                 _ptr(sample_idx), _ptr(tile_budget), _ptr(features_read),
+                                                 _ptr(ws), ws.numel(), _stream(stream))
+    _lib._check("santa_decode_prop_bernoulli", st)
     return ws
 
 

@@ -22,7 +22,7 @@ SAMPLER = {"sys": 0, "strat": 1, "iid": 2}
 
 EXPORTS = [
     "santa_workspace_size", "santa_decode_prop", "santa_decode_prop_sampler", "santa_decode_flash",
-    "santa_decode_flash_sampler", "exact_decode_ref",
+    "santa_decode_flash_sampler", "santa_decode_prop_bernoulli", "exact_decode_ref",
     "santa_set_timing_events", "santa_status_string", "santa_abi_version",
 ]
 
@@ -70,6 +70,9 @@ def load():
     L.santa_decode_flash_sampler.argtypes = [P, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     L.santa_decode_flash_sampler.restype = C.c_int
     L.santa_decode_flash.restype = C.c_int
+    L.santa_decode_prop_bernoulli.argtypes = [P, vp, vp, vp, i32, vp, i32, i32, vp, vp, vp, vp, vp,
+                                              vp, sz, vp]
+    L.santa_decode_prop_bernoulli.restype = C.c_int
     L.exact_decode_ref.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     L.exact_decode_ref.restype = C.c_int
     L.santa_set_timing_events.argtypes = [vp, vp]

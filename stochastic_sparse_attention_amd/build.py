@@ -15,9 +15,11 @@ ARCH = os.environ.get("SANTA_OFFLOAD_ARCH", "gfx950")
 # kernel sources, each compiled once per KV storage type (-DSANTA_KV=...)
 KV_SOURCES = ["santa_prop.hip", "santa_prop_pass1.hip", "santa_flash.hip", "santa_exact.hip"]
 KV_TYPES = {"bf16": "uint16_t", "fp8": "uint8_t", "f32": "float"}
+# kernel sources built for one storage type only (Bernoulli scoring: bf16)
+ONE_TYPE_SOURCES = ["santa_bernoulli.hip"]
 # host sources, compiled once
 HOST_SOURCES = ["santa_api.cpp", "santa_dispatch.cpp"]
-SOURCES = KV_SOURCES + HOST_SOURCES
+SOURCES = KV_SOURCES + ONE_TYPE_SOURCES + HOST_SOURCES
 HEADERS = ["santa_device.h", "santa_score.h", "santa_launch.h", "santa_kernels.h"]
 
 COMMON = [
@@ -55,7 +57,8 @@ def build(verbose=False, jobs=None, out=None, defines=()):
             raise RuntimeError(f"hipcc failed for {src} ({kv or 'host'}):\n{r.stderr}")
         return obj
 
-    jobs_list = [(src, kv) for src in KV_SOURCES for kv in KV_TYPES] + [(src, None) for src in HOST_SOURCES]
+    jobs_list = ([(src, kv) for src in KV_SOURCES for kv in KV_TYPES] +
+                 [(src, None) for src in ONE_TYPE_SOURCES + HOST_SOURCES])
     workers = jobs or min(len(jobs_list), os.cpu_count() or 4, 16)
     with ThreadPoolExecutor(max_workers=workers) as ex:
         objs = list(ex.map(compile_one, jobs_list))

@@ -14,6 +14,7 @@ constexpr int kHeadDimBuilt = 128;
 constexpr int kMaxTiles = 1024;       // reducer and merge: one thread per tile
 constexpr int kMaxSamplesProp = 4096; // prop keeps the selected rows of a head in LDS
 constexpr int kMaxSamples = 65536;
+constexpr int kMaxDraws = 64;         // Bernoulli scoring: ternary draws per query
 
 thread_local void *g_ev_begin = nullptr;
 thread_local void *g_ev_end = nullptr;
@@ -221,6 +222,33 @@ int exact_decode_ref(const santa_problem *p, const void *q, const void *k, const
     return santa::launch_exact(a, hook) == hipSuccess ? SANTA_OK : SANTA_ERR_HIP;
 }
 
+int santa_decode_prop_bernoulli(const santa_problem *p, const void *q, const void *k_features,
+                                const void *v, int32_t S, const float *u, int32_t draws,
+                                int32_t group_mean, const float *u_bern, float *out,
+                                int32_t *sample_idx, int32_t *tile_budget, int32_t *features_read,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    Derived d;
+    int st = validate(p, SANTA_VARIANT_PROP, S, &d);
+    if (st != SANTA_OK) return st;
+    if (draws < 1 || draws > kMaxDraws || (group_mean != 0 && group_mean != 1)) return SANTA_ERR_INVALID;
+    if (p->q_dtype != SANTA_BF16 || p->kv_dtype != SANTA_BF16 || p->page_size != 0 || p->max_seq_len % 4)
+        return SANTA_ERR_UNSUPPORTED;
+    if (p->batch == 0) return SANTA_OK;
+    if (!q || !k_features || !v || !u || !u_bern || !out) return SANTA_ERR_INVALID;
+    if (((uintptr_t)k_features) % 8) return SANTA_ERR_INVALID;
+    santa::Workspace ws;
+    st = check_workspace(p, SANTA_VARIANT_PROP, d, workspace, workspace_bytes, &ws);
+    if (st != SANTA_OK) return st;
+    santa::LaunchArgs a = make_args(p, d, q, k_features, v, S, u, out, sample_idx, tile_budget, ws, stream);
+    a.sampler = santa::kSamplerSys;
+    a.draws = draws;
+    a.group_mean = group_mean;
+    a.u_bern = u_bern;
+    a.features_read = features_read;
+    const santa::TimingHook hook{g_ev_begin, g_ev_end};
+    return santa::launch_prop_bernoulli(a, hook) == hipSuccess ? SANTA_OK : SANTA_ERR_HIP;
+}
+
 int santa_set_timing_events(void *begin_event, void *end_event) {
     if (begin_event && end_event) {
         g_ev_begin = begin_event;
@@ -243,6 +271,6 @@ const char *santa_status_string(int status) {
     }
 }
 
-int santa_abi_version(void) { return 3; }
+int santa_abi_version(void) { return 4; }
 
 }  // extern "C"

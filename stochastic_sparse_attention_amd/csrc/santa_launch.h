@@ -50,6 +50,11 @@ struct LaunchArgs {
     int *tile_budget;
     int kmax;   // prop: visit-list capacity per head
     int sampler;   // prop: kSamplerSys / kSamplerStrat / kSamplerIid
+    // prop on Bernoulli scores: k is feature-major [B, Hkv, d, max_seq_len]
+    int draws;            // ternary draws per query
+    int group_mean;       // 1: one mean query per KV group
+    const float *u_bern;  // [B*Hq or B*Hkv, draws, d] uniforms
+    int *features_read;   // [B*Hkv] or null
     Workspace ws;
     void *stream;
 };
@@ -63,6 +68,10 @@ struct TimingHook {
 hipError_t launch_prop(const LaunchArgs &a, const TimingHook &hook);
 hipError_t launch_flash(const LaunchArgs &a, const TimingHook &hook);
 hipError_t launch_exact(const LaunchArgs &a, const TimingHook &hook);
+// prop with Bernoulli qK^T scores (bf16, contiguous): its pass 1, then the
+// same reducer + pass 2 as launch_prop
+hipError_t launch_prop_bernoulli(const LaunchArgs &a, const TimingHook &hook);
+hipError_t launch_bernoulli_pass1(const LaunchArgs &a, const TimingHook &hook);
 
 // The launchers per KV storage type (uint16_t bf16, uint8_t e4m3, float).
 // Each kernel source is compiled once per type, and every compilation

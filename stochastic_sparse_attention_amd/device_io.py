@@ -28,6 +28,14 @@ class DeviceInputs:
         import torch
         return torch.from_numpy(self.inp.uniforms(S)).to(self.q.device)
 
+    def bernoulli_uniforms(self, draws: int, group_mean: bool):
+        import torch
+        return torch.from_numpy(self.inp.bernoulli_uniforms(draws, group_mean)).to(self.q.device)
+
+    def k_features(self):
+        """K of a contiguous cache transposed per KV head: [B, Hkv, d, n_k]."""
+        return self.k.transpose(-1, -2).contiguous()
+
 
 def _upload(a: np.ndarray, dtype: str, device):
     import torch

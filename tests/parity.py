@@ -44,6 +44,24 @@ def run_prop(dev, S, T=None, sampler="sys", uniforms=None):
     return out.cpu().numpy(), idx.cpu().numpy(), tb.cpu().numpy()
 
 
+def run_prop_bernoulli(dev, S, draws, group_mean, kf=None):
+    torch = _torch()
+    c = dev.inp.cfg
+    BH = c.batch * c.num_q_heads
+    T = dev.problem.s.tile_len
+    max_nt = (c.seq_len + T - 1) // T
+    out = torch.full((BH, c.head_dim), float("nan"), dtype=torch.float32, device=dev.q.device)
+    idx = torch.full((BH, S), -7, dtype=torch.int32, device=dev.q.device)
+    tb = torch.full((BH, max_nt), -7, dtype=torch.int32, device=dev.q.device)
+    fr = torch.full((c.batch * c.num_kv_heads,), -7, dtype=torch.int32, device=dev.q.device)
+    import stochastic_sparse_attention_amd as sa
+    kf = dev.k_features() if kf is None else kf
+    sa.santa_decode_prop_bernoulli(dev.problem, dev.q, kf, dev.v, S, dev.u(S), draws, group_mean,
+                                   dev.bernoulli_uniforms(draws, group_mean), out, idx, tb, fr)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), idx.cpu().numpy(), tb.cpu().numpy(), fr.cpu().numpy()
+
+
 def run_flash(dev, S, sampler="sys"):
     torch = _torch()
     c = dev.inp.cfg
@@ -132,6 +150,51 @@ def check_prop(dev, S, repeat=True, sampler="sys", uniforms=None, oracle_uniform
     if repeat:
         out2, idx2, tb2 = run_prop(dev, S, sampler=sampler, uniforms=uniforms)
         assert np.array_equal(idx, idx2) and np.array_equal(tb, tb2)
+        assert np.array_equal(out.view(np.uint32), out2.view(np.uint32))
+    return rep
+
+
+def _check_budgets(prob, c, S, T, idx, tb, r):
+    seq = prob.seq_lens if prob.seq_lens is not None else np.full(c.batch, c.seq_len)
+    H = c.num_q_heads
+    for bh in range(idx.shape[0]):
+        n = int(seq[bh // H])
+        if n == 0:
+            assert np.all(idx[bh] == -1) and np.all(tb[bh] == 0)
+            continue
+        assert tb[bh].sum() == S
+        own = np.bincount(idx[bh] // T, minlength=tb.shape[1])
+        np.testing.assert_array_equal(own, tb[bh])
+        assert np.all((idx[bh] >= 0) & (idx[bh] < n))
+    clean = ~np.any(idx != r["idx"], axis=1)
+    w = r["tile_counts"].shape[1]
+    assert np.all(tb[:, w:] == 0)
+    np.testing.assert_array_equal(tb[clean, :w], r["tile_counts"][clean])
+
+
+def check_prop_bernoulli(dev, S, draws, group_mean, repeat=True):
+    """prop on Bernoulli qK^T scores against the oracle: the same bar as
+    check_prop, plus the per-group read counts bit-exact."""
+    inp = dev.inp
+    c = inp.cfg
+    T = dev.problem.s.tile_len
+    kf = dev.k_features()
+    out, idx, tb, fr = run_prop_bernoulli(dev, S, draws, group_mean, kf)
+    prob = oracle_problem(dev)
+    ub = inp.bernoulli_uniforms(draws, group_mean)
+    r = O.santa_prop_bernoulli(prob, inp.q, inp.k, inp.v, S, inp.u(S), draws, group_mean, ub)
+    rep = index_report(idx, r["idx"], r["delta"])
+    assert rep["hard"] == 0, rep
+    _check_budgets(prob, c, S, T, idx, tb, r)
+    np.testing.assert_array_equal(fr, O.bernoulli_features(prob, inp.q, draws, group_mean, ub))
+    rp = O.replay(prob, inp.v, S, idx)
+    err = float(np.max(np.abs(out - rp))) if out.size else 0.0
+    assert err <= OUT_TOL, err
+    rep["max_abs_vs_replay"] = err
+    rep["features_read_frac"] = float(fr.mean() / c.head_dim)
+    if repeat:
+        out2, idx2, tb2, fr2 = run_prop_bernoulli(dev, S, draws, group_mean, kf)
+        assert np.array_equal(idx, idx2) and np.array_equal(tb, tb2) and np.array_equal(fr, fr2)
         assert np.array_equal(out.view(np.uint32), out2.view(np.uint32))
     return rep
 

@@ -175,3 +175,26 @@ def test_binding_raises_on_error(lib):
     with pytest.raises(sa.SantaError) as ei:
         sa.santa_workspace_size(prob, "prop", 128)
     assert ei.value.status == UNSUPPORTED
+
+
+def _bern(lib, p, S=128, draws=4, gm=0, kf=DUMMY, ub=DUMMY, ws_bytes=1 << 30):
+    return lib.santa_decode_prop_bernoulli(C.byref(p), DUMMY, kf, DUMMY, S, DUMMY, draws, gm, ub, DUMMY,
+                                           None, None, None, DUMMY, ws_bytes, None)
+
+
+def test_bernoulli_entry_validates_before_launch(lib):
+    """Every case below must fail (or, for B = 0, succeed) before a launch."""
+    p = _problem()
+    assert _bern(lib, p, draws=0) == INVALID
+    assert _bern(lib, p, draws=65) == INVALID
+    assert _bern(lib, p, gm=2) == INVALID
+    assert _bern(lib, _problem(kv_dtype=2)) == UNSUPPORTED                 # e4m3 KV not built here
+    assert _bern(lib, _problem(q_dtype=0, kv_dtype=0)) == UNSUPPORTED      # fp32 not built here
+    assert _bern(lib, _problem(page_size=16, page_table=0x100000, max_pages_per_seq=2048)) == UNSUPPORTED
+    assert _bern(lib, _problem(max_seq_len=1022)) == UNSUPPORTED           # rows not 8-byte aligned
+    assert _bern(lib, p, kf=C.c_void_p(0x100002)) == INVALID
+    assert _bern(lib, p, kf=None) == INVALID
+    assert _bern(lib, p, ub=None) == INVALID
+    assert _bern(lib, p, ws_bytes=16) == WORKSPACE
+    assert _bern(lib, p, S=5000) == UNSUPPORTED
+    assert _bern(lib, _problem(batch=0)) == OK

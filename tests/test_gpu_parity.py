@@ -416,6 +416,50 @@ def test_kv_cache_past_2_pow_31_elements(gpu):
     _say("offsets past 2^31 elements: last request bitwise equal (prop, flash, exact)")
 
 
+# ------------------------------------------------- Bernoulli qK^T + prop
+@pytest.mark.parametrize("T", [64, 256, 1024])
+@pytest.mark.parametrize("draws,group_mean", [(1, 0), (4, 0), (4, 1), (16, 1)])
+def test_bernoulli_prop_small(gpu, T, draws, group_mean):
+    """Ragged last tile (3000 keys), two requests, groups of 4."""
+    import parity
+    cfg = synth.small_config(2, batch=2, seq_len=3000)
+    rep = parity.check_prop_bernoulli(_dev(cfg, 41, gpu, tile_len=T), 128, draws, group_mean)
+    _say("bernoulli T", T, "draws", draws, "mean", group_mean, rep)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (16, 2)])
+@pytest.mark.parametrize("group_mean", [0, 1])
+def test_bernoulli_prop_groups(gpu, hq, hkv, group_mean):
+    import parity
+    cfg = synth.small_config(2, batch=2, seq_len=2048, num_q_heads=hq, num_kv_heads=hkv)
+    rep = parity.check_prop_bernoulli(_dev(cfg, 42, gpu), 64, 4, group_mean)
+    _say("bernoulli G", hq // hkv, "mean", group_mean, rep)
+
+
+def test_bernoulli_prop_empty_ragged_and_tiny(gpu):
+    """Requests of 0, 4, 300 and 2996 keys in a 3000-key cache, and a cache
+    of 4 keys (one partial tile)."""
+    import parity
+    from stochastic_sparse_attention_amd.device_io import to_device
+    cfg = synth.small_config(2, batch=4, seq_len=3000, num_q_heads=8, num_kv_heads=2)
+    inp = synth.make_inputs(cfg, 43)
+    dev = to_device(inp, gpu, seq_lens=np.array([0, 4, 300, 2996], np.int32))
+    for draws, gm in [(4, 0), (4, 1)]:
+        _say("bernoulli empty+ragged", gm, parity.check_prop_bernoulli(dev, 128, draws, gm))
+    cfg = synth.small_config(2, batch=1, seq_len=4, hot=0, sinks=2, num_q_heads=8, num_kv_heads=2)
+    _say("bernoulli 4 keys", parity.check_prop_bernoulli(_dev(cfg, 44, gpu), 16, 2, 0))
+
+
+@pytest.mark.parametrize("cid", [2, 3])
+def test_bernoulli_prop_full_size(gpu, cid):
+    import parity
+    cfg = synth.CONFIGS[cid]
+    dev = _dev(cfg, cid, gpu)
+    for draws, gm in [(4, 0), (4, 1)]:
+        _say("bernoulli full cfg", cid, "mean", gm,
+             parity.check_prop_bernoulli(dev, cfg.S, draws, gm, repeat=cid == 2))
+
+
 # ------------------------------------------------- HIP graph replay
 def test_graph_replays_match_eager(gpu):
     """prop (all three threshold generators), flash (systematic and
