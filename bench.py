@@ -234,6 +234,8 @@ def main(argv=None):
                     help="skip timing prop with the stratified and i.i.d. threshold generators")
     ap.add_argument("--no-flash", action="store_true",
                     help="skip the S2ANTA-flash leg (run where the workload has a flash budget)")
+    ap.add_argument("--no-bernoulli", action="store_true",
+                    help="skip prop on Bernoulli qK^T scores (bf16 contiguous workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 device copies of 256 MiB (known traffic: 256 MiB read and "
                          "256 MiB written each) to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -422,6 +424,40 @@ def main(argv=None):
                     f"tile kernel {np.mean(fk) * 1e3:.2f} us")
                 result["santa_flash"][f"{smp}_us_per_step"] = round(fsms * 1e3, 3)
                 result["santa_flash"][f"{smp}_tile_kernel_us"] = round(float(np.mean(fk)) * 1e3, 3)
+
+    if (not args.no_bernoulli and cfg.kv_dtype == "bf16" and cfg.q_dtype == "bf16" and not cfg.page_size
+            and cfg.seq_len % 4 == 0):
+        # K transposed per KV head (the layout Bernoulli scoring reads), one per rotated copy
+        kfs = [kk.transpose(-1, -2).contiguous() for kk in ks]
+        fr = torch.empty(cfg.batch * cfg.num_kv_heads, dtype=torch.int32, device=dev0)
+        result["bernoulli"] = {"draws": 4, "note": "prop with systematic thresholds on Bernoulli qK^T "
+                               "scores; pass 1 reads only the kept features of a feature-major K"}
+        for gm, name in ((0, "per_head"), (1, "mean_group_query")):
+            ub = dev.bernoulli_uniforms(4, bool(gm))
+
+            def bern_step(i, gm=gm, ub=ub):
+                c = i % ncopy
+                sa.santa_decode_prop_bernoulli(dev.problem, dev.q, kfs[c], vs[c], S, u, 4, gm, ub, out,
+                                               workspace=ws)
+
+            bms, bk = time_steps(bern_step, args.steps, args.warmup, events=True)
+            sa.santa_decode_prop_bernoulli(dev.problem, dev.q, kfs[0], vs[0], S, u, 4, gm, ub, out,
+                                           features_read=fr, workspace=ws)
+            torch.cuda.synchronize()
+            fr_np = fr.cpu().numpy()
+            bb = BM.bernoulli_pass1_bytes(cfg, fr_np, 4, gm, T, seq)
+            bk_ms = float(np.mean(bk))
+            log(f"bench: prop on Bernoulli scores ({name}) {bms * 1e3:.2f} us/step (eager), "
+                f"pass 1 {bk_ms * 1e3:.2f} us, features read {fr_np.mean() / cfg.head_dim:.3f}")
+            result["bernoulli"][name] = {
+                "us_per_step": round(bms * 1e3, 3),
+                "features_read_frac": round(float(fr_np.mean()) / cfg.head_dim, 4),
+                "pass1_kernel_us": round(bk_ms * 1e3, 3),
+                "pass1_bytes": bb,
+                "pass1_GB/s": round(bb / (bk_ms * 1e-3) / 1e9, 1),
+                "speedup_vs_exact_scores": round(ms_eager / bms, 3),
+            }
+        del kfs
 
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")

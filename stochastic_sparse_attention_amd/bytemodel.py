@@ -6,6 +6,8 @@ move), per kernel and per step.
         reducer: tile stats read + visit records
         pass 2:  stash re-read of the tiles with S_t > 0 + S V rows per q head
                  (counted per sample) + output
+  prop on Bernoulli scores, pass 1: the kept features of K only (key
+                 design 4), the same stash, stats and q, and the uniforms
   flash tile:    K + S V rows per q head + partials (m, Z, o_t) written
   exact:         K + V (every row once) + partials
 
@@ -47,6 +49,18 @@ def prop_pass1_bytes(cfg, T=None, seq_lens=None) -> int:
     stats = int(num_tiles(n, T).sum()) * H * 2 * F32
     q = cfg.batch * H * cfg.head_dim * elem_bytes(cfg.q_dtype)
     return kv_bytes(cfg, seq_lens) + stash + stats + q
+
+
+def bernoulli_pass1_bytes(cfg, features_read, draws, group_mean, T=None, seq_lens=None) -> int:
+    """Pass 1 on Bernoulli qK^T scores: of K only the kept features of each
+    KV group (features_read [B*Hkv], each a run of n_k values), then the same
+    stash, stats and q as pass 1, plus the ternary draws' uniforms."""
+    n = _lens(cfg, seq_lens)
+    fr = np.asarray(features_read, np.int64).reshape(cfg.batch, cfg.num_kv_heads)
+    k = int((fr.sum(axis=1) * n).sum()) * elem_bytes(cfg.kv_dtype)
+    owners = cfg.batch * (cfg.num_kv_heads if group_mean else cfg.num_q_heads)
+    uniforms = owners * draws * cfg.head_dim * F32
+    return prop_pass1_bytes(cfg, T, seq_lens) - kv_bytes(cfg, seq_lens) + k + uniforms
 
 
 def stash_reread_bytes(tile_budget: np.ndarray, cfg, T=None, seq_lens=None) -> int:

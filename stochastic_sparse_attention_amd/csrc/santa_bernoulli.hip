@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kBlock) void bernoulli_pass1_kernel(
     for (int qh = 0; qh < NQ; ++qh)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[qh][e] = 0.f;
-    constexpr int U = 4;                         // features in flight per thread
+    constexpr int U = 8;                         // features in flight per thread
     for (int kk = fs; kk < m; kk += U * FP) {
         u32x2 raw[U];
         int fi[U];

@@ -38,3 +38,14 @@ def test_v_row_fraction_counts_distinct_rows():
     cfg = synth.small_config(2, seq_len=1000, num_q_heads=4, num_kv_heads=1)
     idx = np.array([[1, 1, 2], [2, 3, 3], [5, 5, 5], [1, 2, 3]])
     assert BM.v_row_fraction(idx, cfg) == 4 / 1000
+
+
+def test_bernoulli_pass1_bytes():
+    """All features kept: pass 1's bytes plus the uniforms; half kept: half of K less."""
+    from stochastic_sparse_attention_amd import bytemodel as BM
+    cfg = synth.CONFIGS[2]
+    G, d = 8, cfg.head_dim
+    full = BM.bernoulli_pass1_bytes(cfg, np.full(G, d), 4, False)
+    assert full == BM.prop_pass1_bytes(cfg) + 32 * 4 * d * 4
+    half = BM.bernoulli_pass1_bytes(cfg, np.full(G, d // 2), 4, True)
+    assert half == BM.prop_pass1_bytes(cfg) - BM.kv_bytes(cfg) // 2 + 8 * 4 * d * 4
