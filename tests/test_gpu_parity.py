@@ -462,8 +462,9 @@ def test_bernoulli_prop_full_size(gpu, cid):
 
 # ------------------------------------------------- HIP graph replay
 def test_graph_replays_match_eager(gpu):
-    """prop (all three threshold generators), flash (systematic and
-    stratified) and exact decode captured in one HIP graph: every replay,
+    """prop (all three threshold generators, and on Bernoulli scores with the
+    mean group query), flash (systematic and stratified) and exact decode
+    captured in one HIP graph: every replay,
     with eager work and synchronisations in between, gives results bitwise
     equal to the eager calls."""
     import torch
@@ -479,7 +480,9 @@ def test_graph_replays_match_eager(gpu):
     UF, uuf = dev.u(SF), dev.uniforms(SF)
     wsf = torch.empty(sa.santa_workspace_size(dev.problem, "flash", SF), dtype=torch.uint8, device=gpu)
     outs = {k: torch.empty((BH, 128), dtype=torch.float32, device=gpu)
-            for k in ("sys", "strat", "iid", "exact", "flash", "flash_strat")}
+            for k in ("sys", "strat", "iid", "exact", "flash", "flash_strat", "bernoulli")}
+    kf, ub = dev.k_features(), dev.bernoulli_uniforms(4, True)
+    fr = torch.empty(cfg.batch * cfg.num_kv_heads, dtype=torch.int32, device=gpu)
     idx = torch.empty((BH, S), dtype=torch.int32, device=gpu)
     tb = torch.empty((BH, max_nt), dtype=torch.int32, device=gpu)
 
@@ -491,11 +494,13 @@ def test_graph_replays_match_eager(gpu):
         sa.santa_decode_flash(dev.problem, dev.q, dev.k, dev.v, SF, UF, outs["flash"], workspace=wsf)
         sa.santa_decode_flash_sampler(dev.problem, dev.q, dev.k, dev.v, SF, "strat", uuf, outs["flash_strat"],
                                       workspace=wsf)
+        sa.santa_decode_prop_bernoulli(dev.problem, dev.q, kf, dev.v, S, U, 4, 1, ub, outs["bernoulli"],
+                                       features_read=fr, workspace=ws)
 
     step()
     torch.cuda.synchronize()
     ref = {k: v.clone() for k, v in outs.items()}
-    ref_idx, ref_tb = idx.clone(), tb.clone()
+    ref_idx, ref_tb, ref_fr = idx.clone(), tb.clone(), fr.clone()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
@@ -508,6 +513,7 @@ def test_graph_replays_match_eager(gpu):
             v.fill_(float("nan"))
         idx.fill_(-5)
         tb.fill_(-5)
+        fr.fill_(-5)
         scratch.mul_(1.0001)                      # eager work between replays
         torch.cuda.synchronize()
         g.replay()
@@ -515,4 +521,5 @@ def test_graph_replays_match_eager(gpu):
         for k in outs:
             assert torch.equal(outs[k].view(torch.int32), ref[k].view(torch.int32)), (rep, k)
         assert torch.equal(idx, ref_idx) and torch.equal(tb, ref_tb), rep
+        assert torch.equal(fr, ref_fr), rep
     _say("graph replays match eager")
