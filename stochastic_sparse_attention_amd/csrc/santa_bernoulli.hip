@@ -58,13 +58,25 @@ __global__ __launch_bounds__(kBlock) void bernoulli_pass1_kernel(
     __shared__ __align__(16) float part[FP][NQ][T];   // per-slot partial dots, then x and e
 
     // ---- the ternary queries: a, then c_i = sign(q_i) * #{r : fl(u a) < |q_i|}
+    // (the first RP draws' uniforms load together with the query: they do
+    // not depend on a)
     float qv[NE];
+    constexpr int RP = 8;                        // draws whose uniforms load with the query
+    float upre[NE][RP];
 #pragma unroll
     for (int k = 0; k < NE; ++k) {
         const int e = tid + k * kBlock;
         qv[k] = 0.f;
+#pragma unroll
+        for (int r = 0; r < RP; ++r) upre[k][r] = 0.f;
         if (e < NQ * kHeadDim) {
             const int qh = e / kHeadDim, i = e % kHeadDim;
+            const size_t owner = MEAN ? (size_t)b * num_kv_heads + g
+                                      : (size_t)b * num_q_heads + (size_t)g * G + qh;
+            const float *u = ub + owner * (size_t)draws * kHeadDim + i;
+#pragma unroll
+            for (int r = 0; r < RP; ++r)
+                if (r < draws) upre[k][r] = u[(size_t)r * kHeadDim];
             const uint16_t *qrow = q + ((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim + i;
             if (MEAN) {
                 float s = bf16_lo(qrow[0]);
@@ -90,7 +102,10 @@ __global__ __launch_bounds__(kBlock) void bernoulli_pass1_kernel(
             const float *u = ub + owner * (size_t)draws * kHeadDim + i;
             const float mag = fabsf(qv[k]);
             int kept_draws = 0;
-            for (int r = 0; r < draws; ++r) kept_draws += (u[(size_t)r * kHeadDim] * a < mag) ? 1 : 0;
+#pragma unroll
+            for (int r = 0; r < RP; ++r)
+                if (r < draws) kept_draws += (upre[k][r] * a < mag) ? 1 : 0;
+            for (int r = RP; r < draws; ++r) kept_draws += (u[(size_t)r * kHeadDim] * a < mag) ? 1 : 0;
             const int c = qv[k] > 0.f ? kept_draws : (qv[k] < 0.f ? -kept_draws : 0);
             cq[i][qh] = (float)c;
         }
