@@ -762,3 +762,29 @@ def test_bernoulli_group_union_and_mean_query():
     x0, _ = O.bernoulli_logits(prob, q, k, 1, True, ug, 0, 0)
     x1, _ = O.bernoulli_logits(prob, q, k, 1, True, ug, 0, 1)
     assert x0.tolist() == x1.tolist() == [1.0 - 2.0 + 8.0, 0.5 + 1.0 - 2.0]
+
+
+@pytest.mark.parametrize("draws", [1, 2])
+def test_bernoulli_variance_closed_form(draws):
+    """Var of the score estimate = scale^2 (a/draws)^2 sum_i K_i^2 draws p_i (1 - p_i)
+    for independent draws.  With q = [a, q_1], feature 0 is always kept and
+    all of the variance comes from feature 1 (p = k/N on the midpoint grid);
+    enumerating every draw's uniform over the N midpoints gives the exact
+    mean and variance: draws times fewer ternary values each of weight a/draws."""
+    N, a, k1 = 16, 2.0, 5
+    p = k1 / N
+    q = np.array([a, -a * p], np.float32).reshape(1, 1, 2)
+    K = np.array([[[[0.75, 1.5]]]], np.float32)
+    prob = O.Problem(1, 1, 1, 2, 1, q_dtype="f32", kv_dtype="f32", scale=0.5, tile_len=64)
+    mids = (np.arange(N) + 0.5) / N
+    xs = []
+    for combo in np.array(np.meshgrid(*([mids] * draws), indexing="ij")).reshape(draws, -1).T:
+        ub = np.zeros((1, draws, 2), np.float32)
+        ub[0, :, 1] = combo
+        x, _ = O.bernoulli_logits(prob, q, K, draws, False, ub, 0, 0)
+        xs.append(x[0])
+    xs = np.array(xs)
+    exact = 0.5 * (a * 0.75 - a * p * 1.5)
+    var = 0.5 ** 2 * (a / draws) ** 2 * 1.5 ** 2 * draws * p * (1 - p)
+    np.testing.assert_allclose(xs.mean(), exact, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(xs.var(), var, rtol=1e-12, atol=0)
