@@ -53,14 +53,16 @@ def prop_pass1_bytes(cfg, T=None, seq_lens=None) -> int:
 
 def bernoulli_pass1_bytes(cfg, features_read, draws, group_mean, T=None, seq_lens=None) -> int:
     """Pass 1 on Bernoulli qK^T scores: of K only the kept features of each
-    KV group (features_read [B*Hkv], each a run of n_k values), then the same
-    stash, stats and q as pass 1, plus the ternary draws' uniforms."""
+    KV group (features_read [B*Hkv], each a run of n_k values), the stash
+    (one row per head, or per group with the mean query, whose G rows are
+    equal), the same stats and q as pass 1, and the ternary draws' uniforms."""
     n = _lens(cfg, seq_lens)
     fr = np.asarray(features_read, np.int64).reshape(cfg.batch, cfg.num_kv_heads)
     k = int((fr.sum(axis=1) * n).sum()) * elem_bytes(cfg.kv_dtype)
     owners = cfg.batch * (cfg.num_kv_heads if group_mean else cfg.num_q_heads)
     uniforms = owners * draws * cfg.head_dim * F32
-    return prop_pass1_bytes(cfg, T, seq_lens) - kv_bytes(cfg, seq_lens) + k + uniforms
+    stash_saved = int(n.sum()) * (cfg.num_q_heads - cfg.num_kv_heads) * F32 if group_mean else 0
+    return prop_pass1_bytes(cfg, T, seq_lens) - kv_bytes(cfg, seq_lens) + k + uniforms - stash_saved
 
 
 def stash_reread_bytes(tile_budget: np.ndarray, cfg, T=None, seq_lens=None) -> int:

@@ -245,6 +245,8 @@ int santa_decode_prop_bernoulli(const santa_problem *p, const void *q, const voi
     a.group_mean = group_mean;
     a.u_bern = u_bern;
     a.features_read = features_read;
+    // with the mean query the group's heads share its first head's stash row
+    a.stash_shift = group_mean ? (d.group == 8 ? 3 : d.group == 4 ? 2 : d.group == 2 ? 1 : 0) : 0;
     const santa::TimingHook hook{g_ev_begin, g_ev_end};
     return santa::launch_prop_bernoulli(a, hook) == hipSuccess ? SANTA_OK : SANTA_ERR_HIP;
 }

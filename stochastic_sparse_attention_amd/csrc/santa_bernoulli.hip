@@ -12,7 +12,8 @@
 //
 // The kernel writes the stash and the tile statistics in exactly the format
 // of the exact-score pass 1 (stash e_j = exp(scale * (x_j - m_t)), stats
-// (m_t, Z_t) with x unscaled), so the reducer and pass 2 run unchanged.
+// (m_t, Z_t) with x unscaled), so the reducer and pass 2 run unchanged; with
+// the mean query the G equal stash rows of a group are written once.
 #include "santa_kernels.h"
 
 namespace santa {
@@ -205,8 +206,10 @@ __global__ __launch_bounds__(kBlock) void bernoulli_pass1_kernel(
         }
     }
     __syncthreads();
-    // stash rows of all G heads (with the mean query they are equal) and stats
-    for (int hl = w; hl < G; hl += kWavesPerBlock) {
+    // stash rows: one per head, or with the mean query one per group (the
+    // group's first head's row, which the sampler reads for all its heads);
+    // stats for every head
+    for (int hl = w; hl < (MEAN ? 1 : G); hl += kWavesPerBlock) {
         const int qh = MEAN ? 0 : hl;
         float *srow = stash + ((size_t)b * num_q_heads + (size_t)g * G + hl) * ((size_t)max_nt * T) + t0;
         for (int j4 = 4 * lane; j4 < T; j4 += 256)

@@ -55,6 +55,7 @@ struct LaunchArgs {
     int group_mean;       // 1: one mean query per KV group
     const float *u_bern;  // [B*Hq or B*Hkv, draws, d] uniforms
     int *features_read;   // [B*Hkv] or null
+    int stash_shift;      // prop: 1 << stash_shift consecutive heads share one stash row
     Workspace ws;
     void *stream;
 };

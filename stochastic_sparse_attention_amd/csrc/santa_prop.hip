@@ -382,7 +382,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(LIST
     const KV *__restrict__ v, KVLayout L, const int *__restrict__ seq_lens, int batch, int num_q_heads,
     int G, int S, int max_nt, int kcap, int sampler, const float *__restrict__ u, float scale,
     const float *__restrict__ stash, const float2 *__restrict__ stats, float *__restrict__ out,
-    int *__restrict__ sample_idx, int *__restrict__ tile_budget) {
+    int *__restrict__ sample_idx, int *__restrict__ tile_budget, int stash_shift) {
     constexpr int SB = NW * kWave;                  // threads per workgroup
     extern __shared__ __align__(16) unsigned char smem[];
     // stratified / i.i.d.: the sorted thresholds first (padded to a power of
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(LIST
         float e[EPL2];
         // whole slice, unconditionally: pass 1 writes every tile in full,
         // with 0 past the sequence end
-        load_stash<EPL2>(stash + (size_t)bh * max_nt * T + start + gl * EPL2, e);
+        load_stash<EPL2>(stash + (size_t)((bh >> stash_shift) << stash_shift) * max_nt * T + start + gl * EPL2, e);
         float run = 0.f;
 #pragma unroll
         for (int qq = 0; qq < EPL2; ++qq) {
@@ -742,7 +742,8 @@ static hipError_t launch_sample_t(const LaunchArgs &a, const TimingHook &) {
         }
         hipLaunchKernelGGL(kernel, dim3((unsigned)BH), dim3(nw * kWave), lds, st, (const KV *)a.v, L, a.seq_lens,
                            a.batch, a.num_q_heads, G, a.S, max_nt, a.kmax, a.sampler, a.u, a.scale,
-                           (const float *)stash, (const float2 *)stats, a.out, a.sample_idx, a.tile_budget);
+                           (const float *)stash, (const float2 *)stats, a.out, a.sample_idx, a.tile_budget,
+                           a.stash_shift);
         return hipGetLastError();
     };
     if (a.sampler != kSamplerSys)

@@ -41,11 +41,13 @@ def test_v_row_fraction_counts_distinct_rows():
 
 
 def test_bernoulli_pass1_bytes():
-    """All features kept: pass 1's bytes plus the uniforms; half kept: half of K less."""
+    """All features kept: pass 1's bytes plus the uniforms; half kept with the
+    mean query: half of K and three quarters of the stash less."""
     from stochastic_sparse_attention_amd import bytemodel as BM
     cfg = synth.CONFIGS[2]
     G, d = 8, cfg.head_dim
     full = BM.bernoulli_pass1_bytes(cfg, np.full(G, d), 4, False)
     assert full == BM.prop_pass1_bytes(cfg) + 32 * 4 * d * 4
     half = BM.bernoulli_pass1_bytes(cfg, np.full(G, d // 2), 4, True)
-    assert half == BM.prop_pass1_bytes(cfg) - BM.kv_bytes(cfg) // 2 + 8 * 4 * d * 4
+    stash_saved = 32768 * (32 - 8) * 4          # the mean query writes one stash row per group
+    assert half == BM.prop_pass1_bytes(cfg) - BM.kv_bytes(cfg) // 2 + 8 * 4 * d * 4 - stash_saved
