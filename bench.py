@@ -235,7 +235,7 @@ def main(argv=None):
     ap.add_argument("--no-flash", action="store_true",
                     help="skip the S2ANTA-flash leg (run where the workload has a flash budget)")
     ap.add_argument("--no-bernoulli", action="store_true",
-                    help="skip prop on Bernoulli qK^T scores (bf16 contiguous workloads)")
+                    help="skip prop on Bernoulli qK^T scores (contiguous bf16 and e4m3 workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 device copies of 256 MiB (known traffic: 256 MiB read and "
                          "256 MiB written each) to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -425,8 +425,8 @@ def main(argv=None):
                 result["santa_flash"][f"{smp}_us_per_step"] = round(fsms * 1e3, 3)
                 result["santa_flash"][f"{smp}_tile_kernel_us"] = round(float(np.mean(fk)) * 1e3, 3)
 
-    if (not args.no_bernoulli and cfg.kv_dtype == "bf16" and cfg.q_dtype == "bf16" and not cfg.page_size
-            and cfg.seq_len % 4 == 0):
+    if (not args.no_bernoulli and cfg.kv_dtype in ("bf16", "fp8") and cfg.q_dtype == "bf16"
+            and not cfg.page_size and cfg.seq_len % 4 == 0):
         # K transposed per KV head (the layout Bernoulli scoring reads), one per rotated copy
         kfs = [kk.transpose(-1, -2).contiguous() for kk in ks]
         fr = torch.empty(cfg.batch * cfg.num_kv_heads, dtype=torch.int32, device=dev0)

@@ -214,11 +214,13 @@ int exact_decode_ref(const santa_problem *p, const void *q, const void *k, const
  * passed feature-major.  The reducer and pass 2 are those of
  * santa_decode_prop (systematic thresholds).
  *
- * Built for (else SANTA_ERR_UNSUPPORTED): q_dtype = kv_dtype = SANTA_BF16,
- * page_size = 0 (seq_lens may be given), max_seq_len % 4 == 0.
- *   k_features   [B, Hkv, d, max_seq_len] bf16, 8-byte aligned (else
- *                SANTA_ERR_INVALID): K transposed per KV head
- *   v            [B, Hkv, max_seq_len, d] bf16 (the usual layout)
+ * Built for (else SANTA_ERR_UNSUPPORTED): q_dtype = SANTA_BF16 with kv_dtype
+ * SANTA_BF16 or SANTA_FP8_E4M3, page_size = 0 (seq_lens may be given),
+ * max_seq_len % 4 == 0.
+ *   k_features   [B, Hkv, d, max_seq_len] kv_dtype, 8-byte (bf16) or 4-byte
+ *                (e4m3) aligned (else SANTA_ERR_INVALID): K transposed per
+ *                KV head
+ *   v            [B, Hkv, max_seq_len, d] kv_dtype (the usual layout)
  *   draws        ternary draws per query, 1..64 (else SANTA_ERR_INVALID)
  *   group_mean   0: every q head draws its own ternary query, and its KV
  *                group reads the union of their kept features.  1: the fp32

@@ -231,11 +231,13 @@ int santa_decode_prop_bernoulli(const santa_problem *p, const void *q, const voi
     int st = validate(p, SANTA_VARIANT_PROP, S, &d);
     if (st != SANTA_OK) return st;
     if (draws < 1 || draws > kMaxDraws || (group_mean != 0 && group_mean != 1)) return SANTA_ERR_INVALID;
-    if (p->q_dtype != SANTA_BF16 || p->kv_dtype != SANTA_BF16 || p->page_size != 0 || p->max_seq_len % 4)
+    if (p->q_dtype != SANTA_BF16 || (p->kv_dtype != SANTA_BF16 && p->kv_dtype != SANTA_FP8_E4M3) ||
+        p->page_size != 0 || p->max_seq_len % 4)
         return SANTA_ERR_UNSUPPORTED;
     if (p->batch == 0) return SANTA_OK;
     if (!q || !k_features || !v || !u || !u_bern || !out) return SANTA_ERR_INVALID;
-    if (((uintptr_t)k_features) % 8) return SANTA_ERR_INVALID;
+    // 4 keys of a feature per lane load: 8 bytes of bf16, 4 of e4m3
+    if (((uintptr_t)k_features) % (p->kv_dtype == SANTA_BF16 ? 8 : 4)) return SANTA_ERR_INVALID;
     santa::Workspace ws;
     st = check_workspace(p, SANTA_VARIANT_PROP, d, workspace, workspace_bytes, &ws);
     if (st != SANTA_OK) return st;

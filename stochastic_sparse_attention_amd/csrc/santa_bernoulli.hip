@@ -7,8 +7,9 @@
 // probability |q_i| / a and the sign of q_i (kept when fl32(u * a) < |q_i|);
 // with c_i the sum of the draws, (a / draws) * sum_i c_i K_{j,i} estimates
 // <q, K_j> without bias.  Only features with c_i != 0 are read, so K is taken
-// feature-major, [B, Hkv, d, max_seq_len] bf16: a kept feature of a tile is
-// one contiguous run of T values, and a dropped one costs no HBM traffic.
+// feature-major, [B, Hkv, d, max_seq_len] (bf16, or OCP e4m3 with bf16
+// queries): a kept feature of a tile is one contiguous run of T values, and a
+// dropped one costs no HBM traffic.
 //
 // The kernel writes the stash and the tile statistics in exactly the format
 // of the exact-score pass 1 (stash e_j = exp(scale * (x_j - m_t)), stats
@@ -25,15 +26,25 @@ __device__ __forceinline__ float wave_total(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_incl_scan(v, 0)), 63));
 }
 
+// 4 consecutive keys of one feature: 8 bytes of bf16 or 4 of e4m3
+template <typename KV> struct Chunk4;
+template <> struct Chunk4<uint16_t> { typedef u32x2 type; };
+template <> struct Chunk4<uint8_t> { typedef uint32_t type; };
+
+__device__ __forceinline__ void widen4(u32x2 r, float (&k)[4]) {
+    k[0] = bf16_lo(r.x); k[1] = bf16_hi(r.x); k[2] = bf16_lo(r.y); k[3] = bf16_hi(r.y);
+}
+__device__ __forceinline__ void widen4(uint32_t r, float (&k)[4]) { e4m3x4_to_f32(r, k); }
+
 // grid: B * Hkv * max_nt workgroups (tile fastest); block: 256 threads.
-//   q   [B, Hq, d] bf16;  kf  [B, Hkv, d, max_seq_len] bf16 (max_seq_len % 4 == 0)
+//   q   [B, Hq, d] bf16;  kf  [B, Hkv, d, max_seq_len] KV (max_seq_len % 4 == 0)
 //   ub  [owners, draws, d] fp32 uniforms, owners = B*Hq (a query per head) or
 //       B*Hkv (MEAN: one mean query per group)
 //   features_read [B*Hkv] (optional): kept features of the group, written by
 //       the tile-0 workgroup (also for an empty request)
-template <int G, int T, bool MEAN>
+template <typename KV, int G, int T, bool MEAN>
 __global__ __launch_bounds__(kBlock) void bernoulli_pass1_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kf, int num_kv_heads, int max_seq_len,
+    const uint16_t *__restrict__ q, const KV *__restrict__ kf, int num_kv_heads, int max_seq_len,
     const int *__restrict__ seq_lens, int num_q_heads, int max_nt, float scale, int draws,
     const float *__restrict__ ub, float *__restrict__ stash, float2 *__restrict__ stats,
     int *__restrict__ features_read) {
@@ -139,7 +150,8 @@ __global__ __launch_bounds__(kBlock) void bernoulli_pass1_kernel(
     const int chunk = tid % CH, fs = tid / CH;
     const int j = t0 + 4 * chunk;
     const bool jin = j < max_seq_len;            // whole chunk in the row (max_seq_len % 4 == 0)
-    const uint16_t *kbase = kf + ((size_t)b * num_kv_heads + g) * kHeadDim * (size_t)max_seq_len + j;
+    const KV *kbase = kf + ((size_t)b * num_kv_heads + g) * kHeadDim * (size_t)max_seq_len + j;
+    typedef typename Chunk4<KV>::type chunk_t;
     float acc[NQ][4];
 #pragma unroll
     for (int qh = 0; qh < NQ; ++qh)
@@ -147,21 +159,22 @@ __global__ __launch_bounds__(kBlock) void bernoulli_pass1_kernel(
         for (int e = 0; e < 4; ++e) acc[qh][e] = 0.f;
     constexpr int U = 8;                         // features in flight per thread
     for (int kk = fs; kk < m; kk += U * FP) {
-        u32x2 raw[U];
+        chunk_t raw[U];
         int fi[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int k = kk + u * FP;
             fi[u] = k < m ? flist[k] : -1;
-            raw[u] = u32x2{0u, 0u};
+            raw[u] = chunk_t{};
             if (fi[u] >= 0 && jin)
                 raw[u] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x2 *>(kbase + (size_t)fi[u] * max_seq_len));
+                    reinterpret_cast<const chunk_t *>(kbase + (size_t)fi[u] * max_seq_len));
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (fi[u] < 0) continue;
-            const float kv[4] = {bf16_lo(raw[u].x), bf16_hi(raw[u].x), bf16_lo(raw[u].y), bf16_hi(raw[u].y)};
+            float kv[4];
+            widen4(raw[u], kv);
 #pragma unroll
             for (int qh = 0; qh < NQ; ++qh) {
                 const float c = cq[fi[u]][qh];
@@ -221,47 +234,56 @@ __global__ __launch_bounds__(kBlock) void bernoulli_pass1_kernel(
     }
 }
 
-template <int G, int T, bool MEAN>
+template <typename KV, int G, int T, bool MEAN>
 static hipError_t launch_bern_t(const LaunchArgs &a, const TimingHook &hook) {
     hipStream_t st = (hipStream_t)a.stream;
     const dim3 grid((unsigned)(a.batch * a.num_kv_heads * a.max_nt));
     if (hook.begin)
-        hipExtLaunchKernelGGL((bernoulli_pass1_kernel<G, T, MEAN>), grid, dim3(kBlock), 0, st,
+        hipExtLaunchKernelGGL((bernoulli_pass1_kernel<KV, G, T, MEAN>), grid, dim3(kBlock), 0, st,
                               (hipEvent_t)hook.begin, (hipEvent_t)hook.end, 0, (const uint16_t *)a.q,
-                              (const uint16_t *)a.k, a.num_kv_heads, a.max_seq_len, a.seq_lens, a.num_q_heads,
+                              (const KV *)a.k, a.num_kv_heads, a.max_seq_len, a.seq_lens, a.num_q_heads,
                               a.max_nt, a.scale, a.draws, a.u_bern, (float *)a.ws.stash, (float2 *)a.ws.stats,
                               a.features_read);
     else
-        hipLaunchKernelGGL((bernoulli_pass1_kernel<G, T, MEAN>), grid, dim3(kBlock), 0, st, (const uint16_t *)a.q,
-                           (const uint16_t *)a.k, a.num_kv_heads, a.max_seq_len, a.seq_lens, a.num_q_heads,
+        hipLaunchKernelGGL((bernoulli_pass1_kernel<KV, G, T, MEAN>), grid, dim3(kBlock), 0, st, (const uint16_t *)a.q,
+                           (const KV *)a.k, a.num_kv_heads, a.max_seq_len, a.seq_lens, a.num_q_heads,
                            a.max_nt, a.scale, a.draws, a.u_bern, (float *)a.ws.stash, (float2 *)a.ws.stats,
                            a.features_read);
     return hipGetLastError();
 }
 
-template <int G, int T>
+template <typename KV, int G, int T>
 static hipError_t launch_bern_m(const LaunchArgs &a, const TimingHook &hook) {
-    return a.group_mean ? launch_bern_t<G, T, true>(a, hook) : launch_bern_t<G, T, false>(a, hook);
+    return a.group_mean ? launch_bern_t<KV, G, T, true>(a, hook) : launch_bern_t<KV, G, T, false>(a, hook);
 }
 
-template <int G>
+template <typename KV, int G>
 static hipError_t launch_bern_g(const LaunchArgs &a, const TimingHook &hook) {
     switch (a.tile_len) {
-        case 64: return launch_bern_m<G, 64>(a, hook);
-        case 128: return launch_bern_m<G, 128>(a, hook);
-        case 256: return launch_bern_m<G, 256>(a, hook);
-        case 512: return launch_bern_m<G, 512>(a, hook);
-        case 1024: return launch_bern_m<G, 1024>(a, hook);
+        case 64: return launch_bern_m<KV, G, 64>(a, hook);
+        case 128: return launch_bern_m<KV, G, 128>(a, hook);
+        case 256: return launch_bern_m<KV, G, 256>(a, hook);
+        case 512: return launch_bern_m<KV, G, 512>(a, hook);
+        case 1024: return launch_bern_m<KV, G, 1024>(a, hook);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename KV>
+static hipError_t launch_bern_kv(const LaunchArgs &a, const TimingHook &hook) {
+    switch (a.group) {
+        case 1: return launch_bern_g<KV, 1>(a, hook);
+        case 2: return launch_bern_g<KV, 2>(a, hook);
+        case 4: return launch_bern_g<KV, 4>(a, hook);
+        case 8: return launch_bern_g<KV, 8>(a, hook);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_bernoulli_pass1(const LaunchArgs &a, const TimingHook &hook) {
-    switch (a.group) {
-        case 1: return launch_bern_g<1>(a, hook);
-        case 2: return launch_bern_g<2>(a, hook);
-        case 4: return launch_bern_g<4>(a, hook);
-        case 8: return launch_bern_g<8>(a, hook);
+    switch (a.kv_dtype) {
+        case kKvBf16: return launch_bern_kv<uint16_t>(a, hook);
+        case kKvFp8: return launch_bern_kv<uint8_t>(a, hook);
         default: return hipErrorInvalidValue;
     }
 }

@@ -25,7 +25,7 @@ hipError_t launch_prop(const LaunchArgs &a, const TimingHook &hook) {
 hipError_t launch_prop_bernoulli(const LaunchArgs &a, const TimingHook &hook) {
     const hipError_t e = launch_bernoulli_pass1(a, hook);
     if (e != hipSuccess) return e;
-    return launch_prop_sample_kv<uint16_t>(a, hook);
+    return launch_sample(a, hook);
 }
 
 hipError_t launch_flash(const LaunchArgs &a, const TimingHook &hook) { SANTA_KV_SWITCH(launch_flash_kv) }

@@ -188,8 +188,10 @@ def test_bernoulli_entry_validates_before_launch(lib):
     assert _bern(lib, p, draws=0) == INVALID
     assert _bern(lib, p, draws=65) == INVALID
     assert _bern(lib, p, gm=2) == INVALID
-    assert _bern(lib, _problem(kv_dtype=2)) == UNSUPPORTED                 # e4m3 KV not built here
     assert _bern(lib, _problem(q_dtype=0, kv_dtype=0)) == UNSUPPORTED      # fp32 not built here
+    assert _bern(lib, _problem(kv_dtype=2), kf=C.c_void_p(0x100002)) == INVALID   # e4m3 rows: 4-byte aligned
+    assert _bern(lib, _problem(kv_dtype=2, page_size=16, page_table=0x100000,
+                               max_pages_per_seq=2048)) == UNSUPPORTED
     assert _bern(lib, _problem(page_size=16, page_table=0x100000, max_pages_per_seq=2048)) == UNSUPPORTED
     assert _bern(lib, _problem(max_seq_len=1022)) == UNSUPPORTED           # rows not 8-byte aligned
     assert _bern(lib, p, kf=C.c_void_p(0x100002)) == INVALID

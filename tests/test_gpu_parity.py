@@ -450,7 +450,17 @@ def test_bernoulli_prop_empty_ragged_and_tiny(gpu):
     _say("bernoulli 4 keys", parity.check_prop_bernoulli(_dev(cfg, 44, gpu), 16, 2, 0))
 
 
-@pytest.mark.parametrize("cid", [2, 3])
+@pytest.mark.parametrize("T", [64, 256])
+def test_bernoulli_prop_fp8_small(gpu, T):
+    """e4m3 K (feature-major) and V with bf16 queries, ragged last tile."""
+    import parity
+    cfg = synth.small_config(7, batch=2, seq_len=3000)
+    dev = _dev(cfg, 45, gpu, tile_len=T)
+    for draws, gm in [(4, 0), (4, 1), (1, 1)]:
+        _say("bernoulli fp8 T", T, "draws", draws, "mean", gm, parity.check_prop_bernoulli(dev, 128, draws, gm))
+
+
+@pytest.mark.parametrize("cid", [2, 3, 7])
 def test_bernoulli_prop_full_size(gpu, cid):
     import parity
     cfg = synth.CONFIGS[cid]
