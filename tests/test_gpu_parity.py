@@ -460,7 +460,7 @@ def test_bernoulli_prop_fp8_small(gpu, T):
         _say("bernoulli fp8 T", T, "draws", draws, "mean", gm, parity.check_prop_bernoulli(dev, 128, draws, gm))
 
 
-@pytest.mark.parametrize("cid", [2, 3, 7])
+@pytest.mark.parametrize("cid", [2, 3, 4, 6, 7])
 def test_bernoulli_prop_full_size(gpu, cid):
     import parity
     cfg = synth.CONFIGS[cid]
