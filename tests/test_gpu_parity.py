@@ -427,13 +427,15 @@ def test_bernoulli_prop_small(gpu, T, draws, group_mean):
     _say("bernoulli T", T, "draws", draws, "mean", group_mean, rep)
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (16, 2)])
+@pytest.mark.parametrize("hq,hkv,T", [(8, 8, 256), (8, 4, 256), (16, 2, 256), (16, 2, 64), (16, 2, 1024)])
 @pytest.mark.parametrize("group_mean", [0, 1])
-def test_bernoulli_prop_groups(gpu, hq, hkv, group_mean):
+def test_bernoulli_prop_groups(gpu, hq, hkv, T, group_mean):
+    """Groups of 1, 2 and 8; G = 8 also at the smallest and largest tiles
+    (the most per-slot partial sums in LDS)."""
     import parity
     cfg = synth.small_config(2, batch=2, seq_len=2048, num_q_heads=hq, num_kv_heads=hkv)
-    rep = parity.check_prop_bernoulli(_dev(cfg, 42, gpu), 64, 4, group_mean)
-    _say("bernoulli G", hq // hkv, "mean", group_mean, rep)
+    rep = parity.check_prop_bernoulli(_dev(cfg, 42, gpu, tile_len=T), 64, 4, group_mean)
+    _say("bernoulli G", hq // hkv, "T", T, "mean", group_mean, rep)
 
 
 def test_bernoulli_prop_empty_ragged_and_tiny(gpu):
