@@ -217,6 +217,14 @@ def cpu_baseline(inp, S, seconds):
             "single_s": single_s, "single_reps": sreps}
 
 
+def exact_problem(sa, dev, cfg, tile_len):
+    """The device inputs' problem with another tile length (same tensors)."""
+    p = dev.problem
+    return sa.Problem(cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.seq_len,
+                      dtype=cfg.q_dtype, kv_dtype=cfg.kv_dtype, scale=p.s.scale, tile_len=tile_len,
+                      seq_lens=p.seq_lens, page_size=cfg.page_size, page_table=p.page_table)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -351,20 +359,31 @@ def main(argv=None):
     }
 
     if not args.no_exact:
-        wse = torch.empty(sa.santa_workspace_size(dev.problem, "exact"), dtype=torch.uint8, device=dev0)
         oute = torch.empty_like(out)
+        # the baseline takes its own best split: tile lengths T, 2T and 4T are
+        # timed and the fastest one is the reference
+        by_tile = {}
+        for TE in sorted({t for t in (T, 2 * T, 4 * T) if t <= 1024}):
+            pe = exact_problem(sa, dev, cfg, TE)
+            wse = torch.empty(sa.santa_workspace_size(pe, "exact"), dtype=torch.uint8, device=dev0)
 
-        def exact_step(i):
-            c = i % ncopy
-            sa.exact_decode_ref(dev.problem, dev.q, ks[c], vs[c], oute, workspace=wse)
+            def exact_step(i, pe=pe, wse=wse):
+                c = i % ncopy
+                sa.exact_decode_ref(pe, dev.q, ks[c], vs[c], oute, workspace=wse)
 
-        ems_eager, ekern = time_steps(exact_step, args.steps, args.warmup, events=True)
+            tms, tk = time_steps(exact_step, args.steps, args.warmup, events=True)
+            by_tile[TE] = (tms, tk, exact_step)
+            log(f"bench: exact with T={TE} {tms * 1e3:.2f} us/step (eager), partial {np.mean(tk) * 1e3:.2f} us")
+        TE = min(by_tile, key=lambda t: by_tile[t][0])
+        ems_eager, ekern, exact_step = by_tile[TE]
         ems_graph, _espread = time_graph(exact_step, ncopy, args.steps, args.warmup)
         ems = ems_eager if args.mode == "eager" else ems_graph
-        eb = BM.exact_step_bytes(cfg, T, seq)
+        eb = BM.exact_step_bytes(cfg, TE, seq)
         log(f"bench: exact {ems * 1e3:.2f} us/step (eager {ems_eager * 1e3:.2f}, graph {ems_graph * 1e3:.2f}), "
-            f"partial {np.mean(ekern) * 1e3:.2f} us")
+            f"T={TE}, partial {np.mean(ekern) * 1e3:.2f} us")
         result["exact_decode_ref"] = {
+            "tile_len": TE,
+            "eager_us_per_step_by_tile_len": {str(t): round(v[0] * 1e3, 3) for t, v in sorted(by_tile.items())},
             "us_per_step": round(ems * 1e3, 3),
             "eager_us_per_step": round(ems_eager * 1e3, 3),
             "graph_us_per_step": round(ems_graph * 1e3, 3),
