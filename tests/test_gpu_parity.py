@@ -314,6 +314,18 @@ def test_exact_small(gpu, cid, kw):
     _say("exact", cid, rep)
 
 
+@pytest.mark.parametrize("cid,kw", [(2, dict(batch=2, seq_len=3000)),
+                                    (5, dict(batch=4, seq_len=4000, min_seq_len=300)),
+                                    (7, dict(batch=2, seq_len=3000))])
+@pytest.mark.parametrize("T", [512, 1024])
+def test_exact_larger_splits(gpu, cid, kw, T):
+    """The exact baseline at the longer splits the benchmark also times
+    (contiguous, paged and e4m3), ragged last tile."""
+    import parity
+    rep = parity.check_exact(_dev(synth.small_config(cid, **kw), 15, gpu, tile_len=T))
+    _say("exact", cid, "T", T, rep)
+
+
 # ------------------------------------------------- e4m3 KV
 @pytest.mark.parametrize("T", [64, 256, 1024])
 def test_fp8_prop_small(gpu, T):
