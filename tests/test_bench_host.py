@@ -1,5 +1,5 @@
-"""Host-side contract of bench.py (no GPU): the single-GPU guard and the
-HBM-traffic lookup."""
+"""Host-side contract of bench.py (no GPU): the single-GPU guard, the
+HBM-traffic lookup and the exact baseline's problem at other splits."""
 import json
 import os
 import subprocess
@@ -31,3 +31,25 @@ def test_traffic_only_for_profiled_workload_and_sources(monkeypatch):
     # a different source hash: no traffic
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
     assert bench.read_traffic("prop_pass1_kernel", cid) is None
+
+
+def test_exact_baseline_problem_keeps_everything_but_the_split():
+    """The exact baseline is timed at other tile lengths on the same tensors:
+    only tile_len may differ from the workload's problem."""
+    import bench
+    import stochastic_sparse_attention_amd as sa
+    from stochastic_sparse_attention_amd import synth
+
+    class Dev:                       # the fields bench.exact_problem reads
+        pass
+    cfg = synth.CONFIGS[4]
+    dev = Dev()
+    dev.problem = sa.Problem(cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.seq_len,
+                             dtype=cfg.q_dtype, kv_dtype=cfg.kv_dtype, scale=0.125, tile_len=cfg.tile_len)
+    p = bench.exact_problem(sa, dev, cfg, 1024)
+    a, b = dev.problem.s, p.s
+    for f, _ in a._fields_:
+        if f == "tile_len":
+            assert (a.tile_len, b.tile_len) == (cfg.tile_len, 1024)
+        else:
+            assert getattr(a, f) == getattr(b, f), f
