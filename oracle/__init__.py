@@ -12,6 +12,10 @@ Functions and their pins (the tests under tests/ hold the checks):
   invert_cdf / sys_thresholds         pinned by hand-derived partitions of U
                                       (tests/golden), one-hot A, S = n_k on a
                                       uniform A, brute-force enumeration
+  cell_edges / prop_cells /           pinned by the hand-derived CDFs of the
+  flash_cells                         golden partitions (global and per tile);
+                                      every oracle threshold lies in its own
+                                      token's cell
   santa_prop (= untiled systematic)   E_U[estimate] = AV by exact breakpoint
                                       enumeration; per-tile counts within
                                       {floor, ceil} of S * tile mass
@@ -69,6 +73,10 @@ def lib():
         L.oracle_softmax_weights.argtypes = [dp, C.c_int, dp, dp]
         L.oracle_softmax_weights.restype = C.c_double
         L.oracle_invert_cdf.argtypes = [dp, C.c_int, dp, C.c_int, ip, dp]
+        L.oracle_cell_edges.argtypes = [dp, C.c_int, ip, C.c_int, dp, dp]
+        L.oracle_prop_cells.argtypes = [P, vp, vp, C.c_int, C.c_int, fp, C.c_int, C.c_int, fp, ip,
+                                        dp, dp, dp]
+        L.oracle_flash_cells.argtypes = [P, vp, vp, C.c_int, C.c_int, fp, ip, dp, dp, dp]
         L.oracle_sys_thresholds.argtypes = [C.c_double, C.c_int, dp]
         L.oracle_strat_thresholds.argtypes = [dp, C.c_int, dp]
         L.oracle_iid_thresholds.argtypes = [dp, C.c_int, dp]
@@ -170,6 +178,50 @@ def invert_cdf(w, t):
     if rc:
         raise ValueError(f"oracle_invert_cdf: {rc}")
     return idx, dl
+
+
+def cell_edges(w, tok):
+    """CDF cells [F(j-1), F(j)) of the tokens `tok` for weights w (NaN
+    outside [0, n))."""
+    w = np.ascontiguousarray(w, np.float64)
+    tok = np.ascontiguousarray(tok, np.int32)
+    lo = np.empty(tok.size, np.float64)
+    hi = np.empty(tok.size, np.float64)
+    rc = lib().oracle_cell_edges(_dptr(w), w.size, _iptr(tok), tok.size, _dptr(lo), _dptr(hi))
+    if rc:
+        raise ValueError(f"oracle_cell_edges: {rc}")
+    return lo, hi
+
+
+def prop_cells(prob: "Problem", q, k, S, u, tok, sampler="sys", draws=0, group_mean=0, ub=None):
+    """For each head and threshold position m: the threshold t_m of prop's
+    generator and the cell [lo, hi) of token tok[bh, m] in the head's
+    (untiled) CDF; on Bernoulli scores when draws > 0.  Returns (thr, lo, hi)
+    [B*Hq, S] (NaN for empty requests and for tokens outside the request)."""
+    BH = prob.batch * prob.num_q_heads
+    u = np.ascontiguousarray(u, np.float32)
+    tok = np.ascontiguousarray(tok, np.int32).reshape(BH, S)
+    thr, lo, hi = (np.empty((BH, S), np.float64) for _ in range(3))
+    ubp = None if ub is None else _fptr(np.ascontiguousarray(ub, np.float32))
+    rc = lib().oracle_prop_cells(prob.ref, _vp(q), _vp(k), S, SAMPLERS[sampler], _fptr(u), int(draws),
+                                 int(group_mean), ubp, _iptr(tok), _dptr(thr), _dptr(lo), _dptr(hi))
+    if rc:
+        raise ValueError(f"oracle_prop_cells: {rc}")
+    return thr, lo, hi
+
+
+def flash_cells(prob: "Problem", q, k, S, u, tok, sampler="sys"):
+    """As prop_cells for flash: position m belongs to tile m // S_f, and the
+    cell is that of tok[bh, m] in the tile's own CDF (NaN outside the tile)."""
+    BH = prob.batch * prob.num_q_heads
+    u = np.ascontiguousarray(u, np.float32)
+    tok = np.ascontiguousarray(tok, np.int32).reshape(BH, S)
+    thr, lo, hi = (np.empty((BH, S), np.float64) for _ in range(3))
+    rc = lib().oracle_flash_cells(prob.ref, _vp(q), _vp(k), S, SAMPLERS[sampler], _fptr(u), _iptr(tok),
+                                  _dptr(thr), _dptr(lo), _dptr(hi))
+    if rc:
+        raise ValueError(f"oracle_flash_cells: {rc}")
+    return thr, lo, hi
 
 
 def sys_thresholds(U, S):

@@ -333,6 +333,41 @@ int oracle_invert_cdf(const double *w, int n, const double *t, int count,
     return 0;
 }
 
+/* ------------------------------------------------------------------ */
+/* O3 -- the CDF cell of a given token: [F(j-1), F(j)) with F(-1) = 0,  */
+/* F(j) = (w_0 + ... + w_j) / sum(w) and F(n-1) := 1, the cells that    */
+/* oracle_invert_cdf inverts [key design 1: J_m = F^{-1}(T_m)].  A       */
+/* threshold selects token j exactly when it lies in j's cell; where     */
+/* several tokens are correct (a threshold within rounding of an edge),  */
+/* they are the tokens whose cells lie that close to it.  Tokens outside */
+/* [0, n) get NaN edges.                                                 */
+/* ------------------------------------------------------------------ */
+int oracle_cell_edges(const double *w, int n, const int *tok, int count, double *lo, double *hi)
+{
+    double *F = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    if (!F) return -2;
+    double z = 0.0;
+    for (int j = 0; j < n; ++j) z += w[j];
+    double run = 0.0;
+    for (int j = 0; j < n; ++j) {
+        run += w[j];
+        F[j] = run / z;
+    }
+    if (n > 0) F[n - 1] = 1.0;
+    for (int m = 0; m < count; ++m) {
+        int j = tok[m];
+        if (j < 0 || j >= n) {
+            lo[m] = NAN;
+            hi[m] = NAN;
+            continue;
+        }
+        lo[m] = (j > 0) ? F[j - 1] : 0.0;
+        hi[m] = F[j];
+    }
+    free(F);
+    return 0;
+}
+
 /* O4 -- systematic thresholds t_m = U + m/S, m = 0..S-1 (R2) [key design 1] */
 void oracle_sys_thresholds(double U, int S, double *t)
 {
@@ -425,9 +460,18 @@ typedef struct {
     const float *ub;
 } bernoulli_args;
 
+/* Optional cell query (all four NULL, or all given): for every head and
+   threshold position m, cell_thr gets the threshold t_m and [cell_lo,
+   cell_hi) the CDF cell of the token cell_tok names at m (any token, e.g.
+   one chosen by another implementation), by oracle_cell_edges. */
+typedef struct {
+    const int *tok;
+    double *thr, *lo, *hi;
+} cell_query;
+
 static int prop_core(const oracle_problem *p, const void *q, const void *k, const void *v,
                      int S, int kind, const float *u, const bernoulli_args *bern, double *out,
-                     int *idx, double *delta, int *tile_cnt)
+                     int *idx, double *delta, int *tile_cnt, const cell_query *cq)
 {
     if (S <= 0 || kind < 0 || kind > 2 || !lengths_ok(p)) return -1;
     if (bern && bern->draws < 1) return -1;
@@ -445,6 +489,13 @@ static int prop_core(const oracle_problem *p, const void *q, const void *k, cons
             }
             if (tile_cnt)
                 for (int i = 0; i < mnt; ++i) tile_cnt[(size_t)bh * mnt + i] = 0;
+            if (cq)
+                for (int m = 0; m < S; ++m) {
+                    size_t o = (size_t)bh * S + m;
+                    cq->thr[o] = NAN;
+                    cq->lo[o] = NAN;
+                    cq->hi[o] = NAN;
+                }
             continue;
         }
         double *x = (double *)malloc(sizeof(double) * (size_t)n);
@@ -484,8 +535,13 @@ static int prop_core(const oracle_problem *p, const void *q, const void *k, cons
                 oracle_iid_thresholds(u01, S, t);
         }
         if (oracle_invert_cdf(e, n, t, S, J, dl) != 0) {
+            /* rejected thresholds: the call fails; no row is read */
 #pragma omp atomic write
             status = -4;
+            for (int m = 0; m < S; ++m) {
+                J[m] = 0;
+                dl[m] = NAN;
+            }
         }
         mean_of_rows(p, v, b, g, J, S, out + (size_t)bh * d);
         if (idx) memcpy(idx + (size_t)bh * S, J, sizeof(int) * (size_t)S);
@@ -494,6 +550,11 @@ static int prop_core(const oracle_problem *p, const void *q, const void *k, cons
             int *tc = tile_cnt + (size_t)bh * mnt;
             for (int i = 0; i < mnt; ++i) tc[i] = 0;
             for (int m = 0; m < S; ++m) tc[J[m] / p->tile_len] += 1;
+        }
+        if (cq) {
+            size_t o = (size_t)bh * S;
+            memcpy(cq->thr + o, t, sizeof(double) * (size_t)S);
+            oracle_cell_edges(e, n, cq->tok + o, S, cq->lo + o, cq->hi + o);
         }
         free(x); free(e); free(t); free(u01); free(J); free(dl);
     }
@@ -504,7 +565,7 @@ int oracle_santa_prop_sampler(const oracle_problem *p, const void *q, const void
                               const void *v, int S, int kind, const float *u, double *out,
                               int *idx, double *delta, int *tile_cnt)
 {
-    return prop_core(p, q, k, v, S, kind, u, NULL, out, idx, delta, tile_cnt);
+    return prop_core(p, q, k, v, S, kind, u, NULL, out, idx, delta, tile_cnt, NULL);
 }
 
 /* S2ANTA-sys prop: the systematic generator of the function above. */
@@ -512,7 +573,7 @@ int oracle_santa_prop(const oracle_problem *p, const void *q, const void *k,
                       const void *v, int S, const float *u, double *out,
                       int *idx, double *delta, int *tile_cnt)
 {
-    return prop_core(p, q, k, v, S, 0, u, NULL, out, idx, delta, tile_cnt);
+    return prop_core(p, q, k, v, S, 0, u, NULL, out, idx, delta, tile_cnt, NULL);
 }
 
 /* S2ANTA-prop (systematic thresholds) on Bernoulli qK^T scores (O13 in
@@ -524,7 +585,28 @@ int oracle_santa_prop_bernoulli(const oracle_problem *p, const void *q, const vo
                                 int *tile_cnt)
 {
     bernoulli_args ba = {draws, group_mean, ub};
-    return prop_core(p, q, k, v, S, 0, u, &ba, out, idx, delta, tile_cnt);
+    return prop_core(p, q, k, v, S, 0, u, &ba, out, idx, delta, tile_cnt, NULL);
+}
+
+/* Cells of given tokens in prop's (untiled) CDF, with the thresholds of
+   the chosen generator; on Bernoulli scores when draws > 0 (then kind must
+   be 0).  tok [B*Hq*S]; thr, lo, hi [B*Hq*S] (NaN for empty requests).
+   Arguments otherwise as for oracle_santa_prop_sampler and
+   oracle_santa_prop_bernoulli. */
+int oracle_prop_cells(const oracle_problem *p, const void *q, const void *k, int S, int kind,
+                      const float *u, int draws, int group_mean, const float *ub, const int *tok,
+                      double *thr, double *lo, double *hi)
+{
+    if (S <= 0 || !lengths_ok(p) || (draws > 0 && kind != 0)) return -1;
+    double *out = (double *)malloc(sizeof(double) * (size_t)p->batch * p->num_q_heads * p->head_dim);
+    if (!out) return -2;
+    /* the estimate itself is not needed: V is replaced by K, which has the
+       same layout, so no V argument is required */
+    bernoulli_args ba = {draws, group_mean, ub};
+    cell_query cq = {tok, thr, lo, hi};
+    int rc = prop_core(p, q, k, k, S, kind, u, draws > 0 ? &ba : NULL, out, NULL, NULL, NULL, &cq);
+    free(out);
+    return rc;
 }
 
 /* ------------------------------------------------------------------ */
@@ -544,9 +626,9 @@ int oracle_santa_prop_bernoulli(const oracle_problem *p, const void *q, const vo
              at t*S_f .. t*S_f + S_f - 1); local thresholds (m + u_m)/S_f
      kind 2  i.i.d.: u as for kind 1; local thresholds = the tile's
              uniforms, sorted */
-int oracle_santa_flash_sampler(const oracle_problem *p, const void *q, const void *k,
-                               const void *v, int S, int kind, const float *u, double *out,
-                               int *idx, double *delta, double *ptile)
+static int flash_core(const oracle_problem *p, const void *q, const void *k, const void *v,
+                      int S, int kind, const float *u, double *out, int *idx, double *delta,
+                      double *ptile, const cell_query *cq)
 {
     if (p->seq_lens || !lengths_ok(p) || kind < 0 || kind > 2) return -1;
     int n = p->max_seq_len, nt = num_tiles(p, n);
@@ -596,8 +678,23 @@ int oracle_santa_flash_sampler(const oracle_problem *p, const void *q, const voi
                     oracle_iid_thresholds(u01, Sf, t);
             }
             if (oracle_invert_cdf(e, len, t, Sf, J, dl) != 0) {
+                /* rejected thresholds: the call fails; no row is read */
 #pragma omp atomic write
                 status = -4;
+                for (int m = 0; m < Sf; ++m) {
+                    J[m] = 0;
+                    dl[m] = NAN;
+                }
+            }
+            if (cq) {
+                /* the tile's own CDF: the cell of the named token relative
+                   to the tile (NaN if the token lies outside the tile) */
+                size_t o = (size_t)bh * S + (size_t)tt * Sf;
+                for (int m = 0; m < Sf; ++m) {
+                    int jl = cq->tok[o + m] - j0;
+                    cq->thr[o + m] = t[m];
+                    oracle_cell_edges(e, len, &jl, 1, cq->lo + o + m, cq->hi + o + m);
+                }
             }
             for (int m = 0; m < Sf; ++m) J[m] += j0;
             mean_of_rows(p, v, b, g, J, Sf, ot + (size_t)tt * d);
@@ -620,12 +717,37 @@ int oracle_santa_flash_sampler(const oracle_problem *p, const void *q, const voi
     return status;
 }
 
+int oracle_santa_flash_sampler(const oracle_problem *p, const void *q, const void *k,
+                               const void *v, int S, int kind, const float *u, double *out,
+                               int *idx, double *delta, double *ptile)
+{
+    return flash_core(p, q, k, v, S, kind, u, out, idx, delta, ptile, NULL);
+}
+
 /* S2ANTA-flash with systematic thresholds. */
 int oracle_santa_flash(const oracle_problem *p, const void *q, const void *k,
                        const void *v, int S, const float *u, double *out,
                        int *idx, double *delta, double *ptile)
 {
-    return oracle_santa_flash_sampler(p, q, k, v, S, 0, u, out, idx, delta, ptile);
+    return flash_core(p, q, k, v, S, 0, u, out, idx, delta, ptile, NULL);
+}
+
+/* Cells of given tokens in flash's tile-local CDFs: position m belongs to
+   tile m / S_f (tile-major, as flash's indices), its threshold is the
+   tile's local one and [lo, hi) is the named token's cell in that tile's
+   own CDF (NaN if the token is not in the tile).  tok, thr, lo, hi
+   [B*Hq*S]; other arguments as for oracle_santa_flash_sampler. */
+int oracle_flash_cells(const oracle_problem *p, const void *q, const void *k, int S, int kind,
+                       const float *u, const int *tok, double *thr, double *lo, double *hi)
+{
+    if (S <= 0 || !lengths_ok(p)) return -1;
+    double *out = (double *)malloc(sizeof(double) * (size_t)p->batch * p->num_q_heads * p->head_dim);
+    if (!out) return -2;
+    cell_query cq = {tok, thr, lo, hi};
+    /* K stands in for V (same layout); the estimate is not needed */
+    int rc = flash_core(p, q, k, k, S, kind, u, out, NULL, NULL, NULL, &cq);
+    free(out);
+    return rc;
 }
 
 /* ------------------------------------------------------------------ */

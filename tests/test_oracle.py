@@ -50,6 +50,89 @@ def test_golden_partition_expectation():
     np.testing.assert_allclose(mean, A @ V, rtol=0, atol=1e-14)
 
 
+def test_cell_edges_golden():
+    """Token j's cell is [F(j-1), F(j)) of the hand-derived CDF, and every
+    hand-derived selection holds its threshold (key design 1: J_m = F^-1(T_m))."""
+    g = _golden("sys_partitions.json")
+    for case in g["cases"]:
+        w, F, S = case["w"], case["F"], case["S"]
+        n = len(w)
+        lo, hi = O.cell_edges(w, np.arange(n))
+        np.testing.assert_allclose(lo, [0.0] + F[:-1], rtol=0, atol=1e-15, err_msg=case["name"])
+        np.testing.assert_allclose(hi, F, rtol=0, atol=1e-15, err_msg=case["name"])
+        lo, hi = O.cell_edges(w, [-1, n])
+        assert np.all(np.isnan(lo)) and np.all(np.isnan(hi))
+        for U, want in case["points"]:
+            t = U + np.arange(S) / S
+            lo, hi = O.cell_edges(w, want)
+            assert np.all((lo <= t) & (t < hi)), (case["name"], U)
+
+
+def _golden_flash_problem():
+    g = _golden("flash_small.json")
+    w = np.asarray(g["w"], float)
+    n, T, S = w.size, g["T"], g["S"]
+    q = np.ones((1, 1, 1), np.float32)
+    k = np.log(w).astype(np.float32).reshape(1, 1, n, 1)
+    prob = O.Problem(1, 1, 1, 1, n, q_dtype="f32", kv_dtype="f32", scale=1.0, tile_len=T)
+    return g, q, k, prob
+
+
+def test_prop_and_flash_cells_golden():
+    """The cells the parity check uses: the untiled CDF for prop, each tile's
+    own CDF for flash (key designs 2 and 3), on the hand-derived case with
+    logits log(w) (so the weights are w up to fp32 rounding of the logs)."""
+    g, q, k, prob = _golden_flash_problem()
+    S, T = g["S"], g["T"]
+    Fg = [0.0] + g["F_global"]
+    tok = np.array([[0, 1, 2, 3]], np.int32)
+    U = np.array([0.05], np.float32)
+    thr, lo, hi = O.prop_cells(prob, q, k, S, U, tok)
+    np.testing.assert_allclose(thr[0], float(U[0]) + np.arange(S) / S, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lo[0], Fg[:4], rtol=0, atol=1e-6)
+    np.testing.assert_allclose(hi[0], Fg[1:], rtol=0, atol=1e-6)
+    # flash: position m belongs to tile m // S_f and sees that tile's CDF
+    Sf = S // 2
+    U = np.array([0.15], np.float32)
+    tok = np.array([[1, 0, 3, 2]], np.int32)
+    thr, lo, hi = O.flash_cells(prob, q, k, S, U, tok)
+    uf = float(U[0]) * 2
+    np.testing.assert_allclose(thr[0], [uf, uf + 1 / Sf, uf, uf + 1 / Sf], rtol=0, atol=1e-15)
+    F0, F1 = [0.0] + g["F_tiles"][0], [0.0] + g["F_tiles"][1]
+    np.testing.assert_allclose(lo[0], [F0[1], F0[0], F1[1], F1[0]], rtol=0, atol=1e-6)
+    np.testing.assert_allclose(hi[0], [F0[2], F0[1], F1[2], F1[1]], rtol=0, atol=1e-6)
+    # a token outside its position's tile has no cell there
+    thr, lo, hi = O.flash_cells(prob, q, k, S, U, np.array([[2, 1, 0, 3]], np.int32))
+    assert np.isnan(lo[0, 0]) and np.isnan(hi[0, 2]) and not np.isnan(lo[0, 1])
+    assert T == 2
+
+
+@pytest.mark.parametrize("sampler", ["sys", "strat", "iid", "bernoulli", "flash"])
+def test_oracle_indices_lie_in_their_cells(sampler):
+    """Every oracle index's cell holds its threshold, and the boundary
+    distance is the distance to the nearer edge of that cell."""
+    inp, prob = _small_inputs(2, seq_len=300, batch=2, tile_len=64)
+    S = 16
+    if sampler == "flash":
+        inp, prob = _small_inputs(2, seq_len=320, batch=2, tile_len=64)
+        S = 20
+        r = O.santa_flash(prob, inp.q, inp.k, inp.v, S, inp.u(S))
+        thr, lo, hi = O.flash_cells(prob, inp.q, inp.k, S, inp.u(S), r["idx"])
+    elif sampler == "bernoulli":
+        ub = inp.bernoulli_uniforms(4, False)
+        r = O.santa_prop_bernoulli(prob, inp.q, inp.k, inp.v, S, inp.u(S), 4, 0, ub)
+        thr, lo, hi = O.prop_cells(prob, inp.q, inp.k, S, inp.u(S), r["idx"], draws=4, group_mean=0, ub=ub)
+    elif sampler == "sys":
+        r = O.santa_prop(prob, inp.q, inp.k, inp.v, S, inp.u(S))
+        thr, lo, hi = O.prop_cells(prob, inp.q, inp.k, S, inp.u(S), r["idx"])
+    else:
+        uu = inp.uniforms(S)
+        r = O.santa_prop_sampler(prob, inp.q, inp.k, inp.v, S, sampler, uu)
+        thr, lo, hi = O.prop_cells(prob, inp.q, inp.k, S, uu, r["idx"], sampler=sampler)
+    assert np.all((lo <= thr) & (thr < hi))
+    np.testing.assert_array_equal(r["delta"], np.minimum(thr - lo, hi - thr))
+
+
 def test_thresholds_closed_form():
     t = O.sys_thresholds(0.03125, 4)
     assert t.tolist() == [0.03125, 0.28125, 0.53125, 0.78125]
