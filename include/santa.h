@@ -35,7 +35,10 @@
  *         paged:      [num_pages, Hkv, page_size, d]; token j of request b
  *                     is row (j % page_size) of page page_table[b][j / page_size]
  *   u     [B*Hq] fp32, u[b*Hq+h] in [0, 1/S)  (one offset per head; a caller
- *         wanting one offset per request replicates it over the heads)
+ *         wanting one offset per request replicates it over the heads).
+ *         The device clamps any other value into [0, u_max], u_max the
+ *         largest float below 1/S (NaN and -0 count as 0), so every call
+ *         places S thresholds in [0, 1)
  *   out   [B, Hq, d] fp32
  *   q head h reads KV head h / (Hq / Hkv)     (grouped-query attention)
  */
@@ -113,7 +116,8 @@ int santa_workspace_size(const santa_problem *p, int32_t variant, int32_t S, siz
  * divides the sum by S.  This equals untiled systematic sampling.
  *
  *   S            samples per head, 1 <= S <= 4096 (larger: SANTA_ERR_UNSUPPORTED)
- *   u            [B*Hq] offsets in [0, 1/S) (not checked on the device)
+ *   u            [B*Hq] offsets in [0, 1/S) (clamped into it on the device,
+ *                see the layouts above)
  *   out          [B, Hq, d] fp32 estimate
  *   sample_idx   [B, Hq, S] int32 or NULL: token selected by threshold m,
  *                in threshold order (repeats mean multiplicity)
@@ -141,7 +145,8 @@ typedef enum {
  * tile's CDF interval for every generator, so sum_t S_t = S.
  *
  *   sampler      a santa_sampler value (else SANTA_ERR_INVALID)
- *   u            SANTA_SAMPLER_SYS: [B*Hq] offsets in [0, 1/S);
+ *   u            SANTA_SAMPLER_SYS: [B*Hq] offsets in [0, 1/S) (clamped as
+ *                for santa_decode_prop);
  *                STRAT and IID: [B*Hq, S] uniforms in [0, 1).  The device
  *                does not check them: values outside the range are clamped
  *                into it (NaN counts as 0).  STRAT and IID thresholds are

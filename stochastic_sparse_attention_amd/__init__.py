@@ -25,6 +25,102 @@ def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
+# ----------------------------------------------------------------------
+# Argument checks before any pointer reaches the library: a tensor of the
+# wrong type, too short, strided or on another device would make the
+# kernels read or write outside it.  Order: dtype, size, layout, device.
+# ----------------------------------------------------------------------
+def _torch_dtypes(code):
+    import torch
+    if code == SANTA_F32:
+        return (torch.float32,)
+    if code == SANTA_BF16:
+        return (torch.bfloat16,)
+    return (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))   # e4m3 bytes
+
+
+def _check_tensor(fn, name, t, dtypes, min_numel, exact=False):
+    """Raise ValueError unless t has one of `dtypes`, at least (or exactly)
+    min_numel elements and is contiguous."""
+    if t is None:
+        raise ValueError(f"{fn}: {name} is required")
+    if not hasattr(t, "data_ptr") or not hasattr(t, "dtype"):
+        raise ValueError(f"{fn}: {name} must be a torch tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{fn}: {name} has dtype {t.dtype}, expected {' or '.join(map(str, dtypes))}")
+    n = t.numel()
+    if (exact and n != min_numel) or n < min_numel:
+        raise ValueError(f"{fn}: {name} has {n} elements, "
+                         f"{'exactly' if exact else 'at least'} {min_numel} required")
+    if not t.is_contiguous():
+        raise ValueError(f"{fn}: {name} must be contiguous")
+
+
+def _check_devices(fn, named):
+    """Every tensor on the same GPU as the first (q)."""
+    dev = named[0][1].device
+    for name, t in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda" or t.device != dev:
+            raise ValueError(f"{fn}: {name} is on {t.device}, expected "
+                             f"{dev if dev.type == 'cuda' else 'a GPU'}")
+
+
+def _check_args(fn, problem, q, k, v, out, extra=()):
+    """q, K, V, out, the problem's own tensors and the call's other
+    arguments (`extra`: (name, tensor or None, dtypes, min_numel)); then all
+    on one GPU."""
+    P = problem
+    B, Hq, Hkv, d, n = P.batch, P.num_q_heads, P.num_kv_heads, P.head_dim, P.max_seq_len
+    import torch
+    _check_tensor(fn, "q", q, _torch_dtypes(P.q_code), B * Hq * d, exact=True)
+    kv = _torch_dtypes(P.kv_code)
+    for name, t in (("k", k), ("v", v)):
+        if P.page_size:
+            page = Hkv * P.page_size * d
+            _check_tensor(fn, name, t, kv, page)
+            if t.numel() % page:
+                raise ValueError(f"{fn}: {name} must hold whole pages of {page} elements")
+        else:
+            _check_tensor(fn, name, t, kv, B * Hkv * n * d, exact=True)
+    _check_tensor(fn, "out", out, (torch.float32,), B * Hq * d)
+    if P.seq_lens is not None:
+        _check_tensor(fn, "seq_lens", P.seq_lens, (torch.int32,), B, exact=True)
+    if P.page_table is not None:
+        _check_tensor(fn, "page_table", P.page_table, (torch.int32,), B * P.max_pages, exact=True)
+    for name, t, dts, need in extra:
+        if t is not None:
+            _check_tensor(fn, name, t, dts, need)
+    _check_devices(fn, [("q", q), ("k", k), ("v", v), ("out", out), ("seq_lens", P.seq_lens),
+                        ("page_table", P.page_table)] + [(name, t) for name, t, _, _ in extra])
+
+
+def _sampled_extra(fn, problem, S, u, sample_idx, tile_budget, u_per_head):
+    import torch
+    P = problem
+    BH = P.batch * P.num_q_heads
+    if u is None:
+        raise ValueError(f"{fn}: u is required")
+    return [("u", u, (torch.float32,), BH * (u_per_head if u_per_head else 1)),
+            ("sample_idx", sample_idx, (torch.int32,), BH * S),
+            ("tile_budget", tile_budget, (torch.int32,), BH * P.max_tiles())]
+
+
+def _ws_bytes(fn, ws, need, device):
+    """Bytes of a caller's workspace tensor (any dtype), checked."""
+    if not hasattr(ws, "data_ptr"):
+        raise ValueError(f"{fn}: workspace must be a torch tensor")
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError(f"{fn}: workspace holds {nbytes} bytes, {need} required")
+    if not ws.is_contiguous():
+        raise ValueError(f"{fn}: workspace must be contiguous")
+    if ws.device != device:
+        raise ValueError(f"{fn}: workspace is on {ws.device}, expected {device}")
+    return nbytes
+
+
 def _stream(stream):
     import torch
     if stream is None:
@@ -41,9 +137,22 @@ class Problem:
         (default: dtype; "fp8" is OCP e4m3 with bf16 q)."""
         codes = {"f32": SANTA_F32, "bf16": SANTA_BF16, "fp8": SANTA_FP8_E4M3}
         dt, kdt = codes[dtype], codes[kv_dtype or dtype]
+        import torch
+        for name, t in (("seq_lens", seq_lens), ("page_table", page_table)):
+            if t is not None and (not hasattr(t, "dtype") or t.dtype != torch.int32):
+                raise ValueError(f"Problem: {name} must be an int32 tensor")
+        if seq_lens is not None and seq_lens.numel() != batch:
+            raise ValueError(f"Problem: seq_lens has {seq_lens.numel()} entries, batch is {batch}")
+        if page_table is not None and (page_table.dim() != 2 or page_table.shape[0] != batch):
+            raise ValueError("Problem: page_table must be [batch, max_pages_per_seq]")
+        if (page_size > 0) != (page_table is not None):
+            raise ValueError("Problem: a paged cache needs a page table, and only it")
         self.seq_lens = seq_lens
         self.page_table = page_table
         max_pages = 0 if page_table is None else int(page_table.shape[1])
+        self.batch, self.num_q_heads, self.num_kv_heads = batch, num_q_heads, num_kv_heads
+        self.head_dim, self.max_seq_len, self.tile_len = head_dim, max_seq_len, tile_len
+        self.q_code, self.kv_code, self.page_size, self.max_pages = dt, kdt, page_size, max_pages
         self.s = santa_problem(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
                                None if seq_lens is None else seq_lens.data_ptr(),
                                dt, kdt, page_size,
@@ -54,6 +163,9 @@ class Problem:
     def ref(self):
         return C.byref(self.s)
 
+    def max_tiles(self):
+        return (self.max_seq_len + self.tile_len - 1) // self.tile_len
+
 
 def santa_workspace_size(problem: Problem, variant: str, S: int = 0) -> int:
     n = C.c_size_t()
@@ -62,19 +174,23 @@ def santa_workspace_size(problem: Problem, variant: str, S: int = 0) -> int:
     return n.value
 
 
-def _workspace(problem, variant, S, workspace, device):
+def _workspace(fn, problem, variant, S, workspace, device):
+    """(workspace tensor, its byte count): the caller's, checked, or a new one."""
+    need = santa_workspace_size(problem, variant, S)
     if workspace is not None:
-        return workspace
+        return workspace, _ws_bytes(fn, workspace, need, device)
     import torch
-    return torch.empty(max(santa_workspace_size(problem, variant, S), 1), dtype=torch.uint8,
-                       device=device)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return ws, ws.numel()
 
 
 def santa_decode_prop(problem: Problem, q, k, v, S, u, out, sample_idx=None, tile_budget=None,
                       workspace=None, stream=None):
-    ws = _workspace(problem, "prop", S, workspace, q.device)
+    fn = "santa_decode_prop"
+    _check_args(fn, problem, q, k, v, out, _sampled_extra(fn, problem, S, u, sample_idx, tile_budget, 0))
+    ws, nb = _workspace(fn, problem, "prop", S, workspace, q.device)
     st = _lib.load().santa_decode_prop(problem.ref, _ptr(q), _ptr(k), _ptr(v), S, _ptr(u), _ptr(out),
-                                       _ptr(sample_idx), _ptr(tile_budget), _ptr(ws), ws.numel(),
+                                       _ptr(sample_idx), _ptr(tile_budget), _ptr(ws), nb,
                                        _stream(stream))
     _lib._check("santa_decode_prop", st)
     return ws
@@ -83,10 +199,15 @@ def santa_decode_prop(problem: Problem, q, k, v, S, u, out, sample_idx=None, til
 def santa_decode_prop_sampler(problem: Problem, q, k, v, S, sampler, u, out, sample_idx=None,
                               tile_budget=None, workspace=None, stream=None):
     """sampler: "sys" (u: [B*Hq] offsets), "strat" or "iid" (u: [B*Hq, S] uniforms)."""
-    ws = _workspace(problem, "prop", S, workspace, q.device)
+    fn = "santa_decode_prop_sampler"
+    if sampler not in SAMPLER:
+        raise ValueError(f"{fn}: sampler must be one of {sorted(SAMPLER)}")
+    _check_args(fn, problem, q, k, v, out,
+                _sampled_extra(fn, problem, S, u, sample_idx, tile_budget, 0 if sampler == "sys" else S))
+    ws, nb = _workspace(fn, problem, "prop", S, workspace, q.device)
     st = _lib.load().santa_decode_prop_sampler(problem.ref, _ptr(q), _ptr(k), _ptr(v), S, SAMPLER[sampler],
                                                _ptr(u), _ptr(out), _ptr(sample_idx), _ptr(tile_budget),
-                                               _ptr(ws), ws.numel(), _stream(stream))
+                                               _ptr(ws), nb, _stream(stream))
     _lib._check("santa_decode_prop_sampler", st)
     return ws
 
@@ -97,21 +218,33 @@ def santa_decode_prop_bernoulli(problem: Problem, q, k_features, v, S, u, draws,
     """prop on Bernoulli qK^T scores.  k_features: K transposed per KV head,
     [B, Hkv, d, max_seq_len] bf16; u_bern: [B*Hq (or B*Hkv with group_mean),
     draws, d] uniforms in [0, 1)."""
-    ws = _workspace(problem, "prop", S, workspace, q.device)
+    import torch
+    fn = "santa_decode_prop_bernoulli"
+    P = problem
+    owners = P.batch * (P.num_kv_heads if group_mean else P.num_q_heads)
+    if u_bern is None:
+        raise ValueError(f"{fn}: u_bern is required")
+    extra = _sampled_extra(fn, P, S, u, sample_idx, tile_budget, 0) + [
+        ("u_bern", u_bern, (torch.float32,), owners * max(int(draws), 1) * P.head_dim),
+        ("features_read", features_read, (torch.int32,), P.batch * P.num_kv_heads)]
+    _check_args(fn, P, q, k_features, v, out, extra)
+    ws, nb = _workspace(fn, problem, "prop", S, workspace, q.device)
     st = _lib.load().santa_decode_prop_bernoulli(problem.ref, _ptr(q), _ptr(k_features), _ptr(v), S, _ptr(u),
                                                  int(draws), int(group_mean), _ptr(u_bern), _ptr(out),
                                                  _ptr(sample_idx), _ptr(tile_budget), _ptr(features_read),
-                                                 _ptr(ws), ws.numel(), _stream(stream))
+                                                 _ptr(ws), nb, _stream(stream))
     _lib._check("santa_decode_prop_bernoulli", st)
     return ws
 
 
 def santa_decode_flash(problem: Problem, q, k, v, S, u, out, sample_idx=None, tile_budget=None,
                        workspace=None, stream=None):
-    ws = _workspace(problem, "flash", S, workspace, q.device)
+    """tile_budget is ignored by the library (every tile takes S / n_t)."""
+    fn = "santa_decode_flash"
+    _check_args(fn, problem, q, k, v, out, _sampled_extra(fn, problem, S, u, sample_idx, None, 0))
+    ws, nb = _workspace(fn, problem, "flash", S, workspace, q.device)
     st = _lib.load().santa_decode_flash(problem.ref, _ptr(q), _ptr(k), _ptr(v), S, _ptr(u), _ptr(out),
-                                        _ptr(sample_idx), _ptr(tile_budget), _ptr(ws), ws.numel(),
-                                        _stream(stream))
+                                        _ptr(sample_idx), None, _ptr(ws), nb, _stream(stream))
     _lib._check("santa_decode_flash", st)
     return ws
 
@@ -119,18 +252,24 @@ def santa_decode_flash(problem: Problem, q, k, v, S, u, out, sample_idx=None, ti
 def santa_decode_flash_sampler(problem: Problem, q, k, v, S, sampler, u, out, sample_idx=None,
                                tile_budget=None, workspace=None, stream=None):
     """sampler: "sys" (u: [B*Hq] offsets), "strat" or "iid" (u: [B*Hq, S] uniforms, tile-major)."""
-    ws = _workspace(problem, "flash", S, workspace, q.device)
+    fn = "santa_decode_flash_sampler"
+    if sampler not in SAMPLER:
+        raise ValueError(f"{fn}: sampler must be one of {sorted(SAMPLER)}")
+    _check_args(fn, problem, q, k, v, out,
+                _sampled_extra(fn, problem, S, u, sample_idx, None, 0 if sampler == "sys" else S))
+    ws, nb = _workspace(fn, problem, "flash", S, workspace, q.device)
     st = _lib.load().santa_decode_flash_sampler(problem.ref, _ptr(q), _ptr(k), _ptr(v), S, SAMPLER[sampler],
-                                                _ptr(u), _ptr(out), _ptr(sample_idx), _ptr(tile_budget),
-                                                _ptr(ws), ws.numel(), _stream(stream))
+                                                _ptr(u), _ptr(out), _ptr(sample_idx), None,
+                                                _ptr(ws), nb, _stream(stream))
     _lib._check("santa_decode_flash_sampler", st)
     return ws
 
 
 def exact_decode_ref(problem: Problem, q, k, v, out, workspace=None, stream=None):
-    ws = _workspace(problem, "exact", 0, workspace, q.device)
+    _check_args("exact_decode_ref", problem, q, k, v, out)
+    ws, nb = _workspace("exact_decode_ref", problem, "exact", 0, workspace, q.device)
     st = _lib.load().exact_decode_ref(problem.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws),
-                                      ws.numel(), _stream(stream))
+                                      nb, _stream(stream))
     _lib._check("exact_decode_ref", st)
     return ws
 

@@ -266,6 +266,20 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// The systematic offset U is meant to lie in [0, 1/S).  Any other value is
+// clamped into [0, u_max], u_max the largest float below 1/S (NaN and -0
+// become +0), so that threshold m stays in [m/S, (m+1)/S) and all S
+// thresholds lie below 1: every position of the index list is written and
+// the budgets sum to S whatever the caller passes.
+__device__ __forceinline__ double clamp_offset(float U, int S) {
+    const double inv = 1.0 / (double)S;
+    float umax = (float)inv;                      // nearest float to 1/S
+    if ((double)umax >= inv) umax = __uint_as_float(__float_as_uint(umax) - 1u);
+    float x = U > 0.f ? U : 0.f;
+    x = x < umax ? x : umax;
+    return (double)x;
+}
+
 // count of thresholds t_m = U + m/S (m = 0..S-1) strictly below x:
 // #{m >= 0 : m < (x - U) S} = ceil((x - U) S), clamped to [0, S]
 // (branch-free; a NaN position counts as 0)

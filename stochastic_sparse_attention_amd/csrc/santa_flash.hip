@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
         int cj[EPL];
         int lmax = 0;
         if constexpr (!LIST) {
-            const double uf = (double)u[bh] * (double)nt;
+            const double uf = clamp_offset(u[bh], S) * (double)nt;
             // per-element local threshold counts #{m : u_f + m/S_f < P_j / Z_t}
             //   = ceil(P_j * a + b), a = S_f / Z_t, b = -u_f S_f (fp32; the
             //   rounding moves a threshold by ~1e-7 of the tile's mass)

@@ -521,7 +521,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(LIST
         int *budget = tile_budget ? tile_budget + (size_t)bh * max_nt : nullptr;
         const ReducerLds R{tstat, tf, tC, tcn};
         if constexpr (!LIST)
-            reduce_head(stp, st, nt, lane, SysCount{(double)u[bh], S}, scale, kcap, vis, budget, max_nt, nvis_sh, R);
+            reduce_head(stp, st, nt, lane, SysCount{clamp_offset(u[bh], S), S}, scale, kcap, vis, budget, max_nt, nvis_sh, R);
         else
             reduce_head(stp, st, nt, lane, ListCount{thr, S, sampler == kSamplerStrat}, scale, kcap, vis, budget,
                         max_nt, nvis_sh, R);

@@ -108,6 +108,31 @@ def test_prop_list_ties_and_clamping(gpu, S):
     for smp in ("strat", "iid"):
         _say(smp, "clamped, S", S, parity.check_prop(dev, S, sampler=smp, uniforms=raw, oracle_uniforms=clamped,
                                                      repeat=False))
+    # systematic offsets outside [0, 1/S): the device clamps them into
+    # [0, u_max], u_max the largest float below 1/S (NaN and -0 as 0)
+    Ur, Uc = sys_offsets_out_of_range(8, S)
+    _say("sys clamped, S", S, parity.check_prop(dev, S, uniforms=Ur, oracle_uniforms=Uc, repeat=False))
+
+
+def sys_offsets_out_of_range(BH, S):
+    """Raw offsets for BH heads (above 1/S, exactly 1/S, 1, negative, NaN,
+    -0, in range) and the values the device is to clamp them to."""
+    inv = np.float32(1.0 / S)
+    umax = inv if float(inv) < 1.0 / S else np.nextafter(inv, np.float32(0))
+    cand = np.array([0.75, inv, 1.0, -0.125, np.nan, -0.0, 0.5 * inv, 2.0 * inv], np.float32)
+    raw = cand[np.arange(BH) % cand.size]
+    clamped = np.where(np.isnan(raw) | (raw <= 0), np.float32(0), np.minimum(raw, umax)).astype(np.float32)
+    return raw, clamped
+
+
+def test_flash_sys_offset_clamping(gpu):
+    """Flash takes the same clamped offset (u_f = U n_t stays below 1/S_f)."""
+    import parity
+    cfg = synth.small_config(3, batch=1, seq_len=4096, num_q_heads=8, num_kv_heads=2)
+    dev = _dev(cfg, 32, gpu)
+    for S in (256, 1024):
+        Ur, Uc = sys_offsets_out_of_range(8, S)
+        _say("flash sys clamped, S", S, parity.check_flash(dev, S, uniforms=Ur, oracle_uniforms=Uc, repeat=False))
 
 
 def test_sampler_variance_ordering(gpu):
@@ -229,8 +254,12 @@ def test_prop_uniform_S_equals_nk_is_mean(gpu):
     inp.k[...] = inp.k[:, :, :1, :]
     dev = to_device(inp, gpu)
     out, idx, tb = parity.run_prop(dev, 1024)
+    # F_j = (j + 1)/1024 exactly, so threshold m = U + m/1024 selects token m:
+    # the list must be 0..1023 in threshold order, not only as a set
+    U = dev.inp.u(1024)
+    assert np.all((U > 1e-6) & (U < 1.0 / 1024 - 1e-6)), U      # no threshold near an edge
     for h in range(4):
-        assert np.array_equal(np.sort(idx[h]), np.arange(1024))
+        assert np.array_equal(idx[h], np.arange(1024)), h
     np.testing.assert_allclose(out, np.broadcast_to(inp.values("v")[0, 0].mean(0), out.shape), atol=1e-5)
 
 
