@@ -47,8 +47,25 @@ class santa_problem(C.Structure):
 _lib = None
 
 
+def hip_runtimes_mapped():
+    """Paths of the HIP runtime libraries mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({line.split()[-1] for line in f if "libamdhip64" in line})
+    except OSError:
+        return []
+
+
 def load():
-    """Load libsanta.so; raises if it is missing (no fallback path exists)."""
+    """Load libsanta.so; raises if it is missing (no fallback path exists).
+
+    The library must run on the HIP runtime that torch uses, since the
+    tensors, their device pointers and the stream all come from torch.
+    torch ships its own libamdhip64 under the same soname as the system one,
+    so torch is imported first: the library's dependency then binds to
+    torch's copy.  Opening the library first would map a second runtime,
+    and every launch would fail on torch's pointers and streams; if two are
+    mapped anyway, loading raises."""
     global _lib
     if _lib is not None:
         return _lib
@@ -56,7 +73,12 @@ def load():
         raise ImportError(
             f"{LIB_PATH} is not built; run `python -m stochastic_sparse_attention_amd.build` "
             "(or __graft_entry__.build()) first")
+    import torch  # noqa: F401  (its HIP runtime first)
     L = C.CDLL(LIB_PATH)
+    runtimes = hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError(f"libsanta: more than one HIP runtime is loaded ({runtimes}); the library must "
+                          "share torch's, so import torch before anything opens libsanta.so")
     P = C.POINTER(santa_problem)
     vp, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
     L.santa_workspace_size.argtypes = [P, i32, i32, C.POINTER(sz)]
