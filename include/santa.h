@@ -58,7 +58,9 @@ typedef enum {
     SANTA_ERR_INVALID = -1,      /* null required pointer, bad size, bad combination */
     SANTA_ERR_UNSUPPORTED = -2,  /* valid but not built: head_dim, dtype, group, tile */
     SANTA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required        */
-    SANTA_ERR_HIP = -4           /* a HIP launch reported an error                    */
+    SANTA_ERR_HIP = -4,          /* a HIP launch reported an error                    */
+    SANTA_ERR_TOO_LARGE = -5     /* santa_decode_prop_static: the problem needs more
+                                    than SANTA_STATIC_SCRATCH_BYTES of workspace     */
 } santa_status;
 
 /* Storage types.  SANTA_FP8_E4M3 is OCP e4m3 (1 sign, 4 exponent bits with
@@ -246,6 +248,30 @@ int santa_decode_prop_bernoulli(const santa_problem *p, const void *q, const voi
                                 int32_t group_mean, const float *u_bern, float *out,
                                 int32_t *sample_idx, int32_t *tile_budget, int32_t *features_read,
                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * santa_decode_prop without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc.  The call allocates nothing: its
+ * workspace is a static device array of SANTA_STATIC_SCRATCH_BYTES (32 MiB)
+ * inside the library, which every GPU the library runs on holds until the
+ * process ends (its address is looked up once per device, on the first call
+ * made with that device current).
+ *   - Problems whose santa_workspace_size(p, SANTA_VARIANT_PROP, S) exceeds
+ *     SANTA_STATIC_SCRATCH_BYTES return SANTA_ERR_TOO_LARGE, launching
+ *     nothing (e.g. the 32k-token, 32/8-head layer fits up to batch 7).
+ *   - All calls on one GPU share that GPU's array.  Calls that overlap in
+ *     time on one GPU (other streams, other threads) race on it and give
+ *     undefined results; calls in one stream are ordered and safe.  Nothing
+ *     in the array has to start at zero: each call writes every entry it
+ *     reads.
+ *   - Arguments, results and every other convention as for
+ *     santa_decode_prop (same kernels, bitwise the same results).
+ */
+#define SANTA_STATIC_SCRATCH_BYTES (32u << 20)
+int santa_decode_prop_static(const santa_problem *p, const void *q, const void *k, const void *v,
+                             int32_t S, const float *u, float *out, int32_t *sample_idx,
+                             int32_t *tile_budget, void *stream);
 
 /*
  * Optional timing hook for benchmarks.  When both events are non-NULL

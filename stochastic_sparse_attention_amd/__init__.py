@@ -16,7 +16,7 @@ from ._lib import SantaError, santa_problem, SANTA_F32, SANTA_BF16, SANTA_FP8_E4
 
 __all__ = [
     "Problem", "santa_workspace_size", "santa_decode_prop", "santa_decode_prop_sampler", "santa_decode_flash",
-    "santa_decode_flash_sampler", "santa_decode_prop_bernoulli",
+    "santa_decode_flash_sampler", "santa_decode_prop_bernoulli", "santa_decode_prop_static",
     "exact_decode_ref", "santa_set_timing_events", "SantaError",
 ]
 
@@ -263,6 +263,17 @@ def santa_decode_flash_sampler(problem: Problem, q, k, v, S, sampler, u, out, sa
                                                 _ptr(ws), nb, _stream(stream))
     _lib._check("santa_decode_flash_sampler", st)
     return ws
+
+
+def santa_decode_prop_static(problem: Problem, q, k, v, S, u, out, sample_idx=None, tile_budget=None,
+                             stream=None):
+    """santa_decode_prop with the library's static device workspace: the
+    call allocates nothing (for code that cannot allocate)."""
+    fn = "santa_decode_prop_static"
+    _check_args(fn, problem, q, k, v, out, _sampled_extra(fn, problem, S, u, sample_idx, tile_budget, 0))
+    st = _lib.load().santa_decode_prop_static(problem.ref, _ptr(q), _ptr(k), _ptr(v), S, _ptr(u), _ptr(out),
+                                              _ptr(sample_idx), _ptr(tile_budget), _stream(stream))
+    _lib._check(fn, st)
 
 
 def exact_decode_ref(problem: Problem, q, k, v, out, workspace=None, stream=None):

@@ -16,13 +16,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("SANTA_LIB") or os.path.join(HERE, "libsanta.so")
 
 SANTA_OK, SANTA_ERR_INVALID, SANTA_ERR_UNSUPPORTED, SANTA_ERR_WORKSPACE, SANTA_ERR_HIP = 0, -1, -2, -3, -4
+SANTA_ERR_TOO_LARGE = -5
+SANTA_STATIC_SCRATCH_BYTES = 32 << 20
 SANTA_F32, SANTA_BF16, SANTA_FP8_E4M3 = 0, 1, 2
 VARIANT = {"prop": 0, "flash": 1, "exact": 2}
 SAMPLER = {"sys": 0, "strat": 1, "iid": 2}
 
 EXPORTS = [
     "santa_workspace_size", "santa_decode_prop", "santa_decode_prop_sampler", "santa_decode_flash",
-    "santa_decode_flash_sampler", "santa_decode_prop_bernoulli", "exact_decode_ref",
+    "santa_decode_flash_sampler", "santa_decode_prop_bernoulli", "exact_decode_ref", "santa_decode_prop_static",
     "santa_set_timing_events", "santa_status_string", "santa_abi_version",
 ]
 
@@ -95,6 +97,8 @@ def load():
     L.santa_decode_prop_bernoulli.argtypes = [P, vp, vp, vp, i32, vp, i32, i32, vp, vp, vp, vp, vp,
                                               vp, sz, vp]
     L.santa_decode_prop_bernoulli.restype = C.c_int
+    L.santa_decode_prop_static.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp]
+    L.santa_decode_prop_static.restype = C.c_int
     L.exact_decode_ref.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     L.exact_decode_ref.restype = C.c_int
     L.santa_set_timing_events.argtypes = [vp, vp]

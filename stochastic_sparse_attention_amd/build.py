@@ -15,8 +15,9 @@ ARCH = os.environ.get("SANTA_OFFLOAD_ARCH", "gfx950")
 # kernel sources, each compiled once per KV storage type (-DSANTA_KV=...)
 KV_SOURCES = ["santa_prop.hip", "santa_prop_pass1.hip", "santa_flash.hip", "santa_exact.hip"]
 KV_TYPES = {"bf16": "uint16_t", "fp8": "uint8_t", "f32": "float"}
-# kernel sources built for one storage type only (Bernoulli scoring: bf16)
-ONE_TYPE_SOURCES = ["santa_bernoulli.hip"]
+# sources built once: Bernoulli scoring (bf16 and e4m3 in one unit) and the
+# allocation-free prop entry point (its static device workspace)
+ONE_TYPE_SOURCES = ["santa_bernoulli.hip", "santa_static.hip"]
 # host sources, compiled once
 HOST_SOURCES = ["santa_api.cpp", "santa_dispatch.cpp"]
 SOURCES = KV_SOURCES + ONE_TYPE_SOURCES + HOST_SOURCES

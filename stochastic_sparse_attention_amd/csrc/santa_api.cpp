@@ -271,10 +271,11 @@ const char *santa_status_string(int status) {
         case SANTA_ERR_UNSUPPORTED: return "unsupported configuration";
         case SANTA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case SANTA_ERR_HIP: return "HIP launch error";
+        case SANTA_ERR_TOO_LARGE: return "problem needs more workspace than the static scratch holds";
         default: return "unknown status";
     }
 }
 
-int santa_abi_version(void) { return 4; }
+int santa_abi_version(void) { return 5; }
 
 }  // extern "C"
