@@ -23,6 +23,13 @@
 
 #include "santa_device.h"
 
+// 64-row steps of a bf16 tile whose K loads are issued together: all four
+// of a 256-row tile (64 KiB per workgroup in flight at once; 92 VGPRs, so
+// 4 workgroups per CU still fit, as many as the 32k batch-1 grid places)
+#ifndef SANTA_BF16_STEPS_IN_FLIGHT
+#define SANTA_BF16_STEPS_IN_FLIGHT 4
+#endif
+
 namespace santa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -68,7 +75,7 @@ struct ScorerMfma {
     static constexpr int NV = 4;
     // steps whose K loads are in flight together: e4m3 rows are half as long,
     // so twice as many steps keep the same bytes in flight
-    static constexpr int CH_MAX = sizeof(KV) == 1 ? 4 : 2;
+    static constexpr int CH_MAX = sizeof(KV) == 1 ? 4 : SANTA_BF16_STEPS_IN_FLIGHT;
     static constexpr int CH = NS < CH_MAX ? NS : CH_MAX;
     static constexpr int kStageVec = kWavesPerBlock * 256;   // LDS staging, 16-byte units (4 KiB per wave)
     bf16x8_t qa[4];
