@@ -96,6 +96,12 @@ CONFIGS = {
     7: Config(7, "Llama-3.1-8B decode layer, 32k context, batch 16, fp8 e4m3 KV", 16, 32, 8, 128, 32768,
               "bf16", "fp8", S=128, tile_len=256, hot=64, sinks=4, S_flash=2048, u_per_request=True,
               variants=("prop", "flash", "exact")),
+    # flat attention (no planted keys, no sinks): the logits are ~N(0, 1),
+    # so A is smooth, nearly every tile takes a threshold and the visit list
+    # runs near its cap (the SANTA notes name flat attention as the case
+    # their analysis does not cover)
+    8: Config(8, "Llama-3.1-8B decode layer, 32k context, batch 1, flat attention", 1, 32, 8, 128, 32768,
+              "bf16", "bf16", S=128, tile_len=256, S_flash=2048, variants=("prop", "flash", "exact")),
 }
 
 

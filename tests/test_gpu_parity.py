@@ -400,6 +400,25 @@ def test_full_size_prop(gpu, cid):
         _say("full flash cfg", cid, parity.check_flash(dev, cfg.S_flash, repeat=False))
 
 
+def test_full_size_flat_attention(gpu):
+    """The 32k batch-1 layer without planted keys or sinks: smooth A, most
+    tiles visited.  prop with the three threshold generators, flash at
+    S = 2048 and the exact decode, each against the oracle."""
+    import parity
+    cfg = synth.CONFIGS[8]
+    _say("generating flat cfg")
+    dev = _dev(cfg, cfg.cid, gpu)
+    for smp in ("sys", "strat", "iid"):
+        rep = parity.check_prop(dev, cfg.S, sampler=smp, repeat=smp == "sys")
+        _say("flat prop", smp, rep)
+    out, idx, tb = parity.run_prop(dev, cfg.S)
+    visited = (tb > 0).sum(1)
+    _say("flat: tiles visited per head", float(visited.mean()), "of", tb.shape[1])
+    assert visited.mean() > 0.5 * tb.shape[1]
+    _say("flat flash", parity.check_flash(dev, cfg.S_flash, repeat=False))
+    _say("flat exact", parity.check_exact(dev, repeat=False))
+
+
 # ------------------------------------------------- offsets past 2^31 elements
 def test_kv_cache_past_2_pow_31_elements(gpu):
     """A KV cache of more than 2^31 elements: 17 requests x 8 KV heads x
