@@ -72,35 +72,45 @@ __global__ __launch_bounds__(kBlock) void bernoulli_pass1_kernel(
     // ---- the ternary queries: a, then c_i = sign(q_i) * #{r : fl(u a) < |q_i|}
     // (the first RP draws' uniforms load together with the query: they do
     // not depend on a)
+    // Every load is issued unconditionally, from indices clamped into range,
+    // and selected afterwards, so that all of them are in flight together
+    // (a load under a per-lane condition becomes a branch that waits for it).
     float qv[NE];
     constexpr int RP = 8;                        // draws whose uniforms load with the query
+    constexpr int QL = MEAN ? G : 1;             // query rows read per entry
     float upre[NE][RP];
+    uint16_t qraw[NE][QL];
+#pragma unroll
+    for (int k = 0; k < NE; ++k) {
+        const int e = min(tid + k * kBlock, NQ * kHeadDim - 1);
+        const int qh = e / kHeadDim, i = e % kHeadDim;
+        const size_t owner = MEAN ? (size_t)b * num_kv_heads + g : (size_t)b * num_q_heads + (size_t)g * G + qh;
+        const float *u = ub + owner * (size_t)draws * kHeadDim + i;
+#pragma unroll
+        for (int r = 0; r < RP; ++r) upre[k][r] = u[(size_t)min(r, draws - 1) * kHeadDim];
+        const uint16_t *qrow = q + ((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim + i;
+#pragma unroll
+        for (int hh = 0; hh < QL; ++hh) qraw[k][hh] = qrow[(size_t)(MEAN ? hh : qh) * kHeadDim];
+    }
 #pragma unroll
     for (int k = 0; k < NE; ++k) {
         const int e = tid + k * kBlock;
-        qv[k] = 0.f;
+        const bool ok = e < NQ * kHeadDim;
+        float qf;
+        if (MEAN) {
+            float s = bf16_lo(qraw[k][0]);
 #pragma unroll
-        for (int r = 0; r < RP; ++r) upre[k][r] = 0.f;
-        if (e < NQ * kHeadDim) {
-            const int qh = e / kHeadDim, i = e % kHeadDim;
-            const size_t owner = MEAN ? (size_t)b * num_kv_heads + g
-                                      : (size_t)b * num_q_heads + (size_t)g * G + qh;
-            const float *u = ub + owner * (size_t)draws * kHeadDim + i;
-#pragma unroll
-            for (int r = 0; r < RP; ++r)
-                if (r < draws) upre[k][r] = u[(size_t)r * kHeadDim];
-            const uint16_t *qrow = q + ((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim + i;
-            if (MEAN) {
-                float s = bf16_lo(qrow[0]);
-                for (int hh = 1; hh < G; ++hh) s = s + bf16_lo(qrow[(size_t)hh * kHeadDim]);
-                qv[k] = s * (1.0f / (float)G);
-            } else {
-                qv[k] = bf16_lo(qrow[(size_t)qh * kHeadDim]);
-            }
+            for (int hh = 1; hh < QL; ++hh) s = s + bf16_lo(qraw[k][hh]);
+            qf = s * (1.0f / (float)G);
+        } else {
+            qf = bf16_lo(qraw[k][0]);
         }
+        qv[k] = ok ? qf : 0.f;
+#pragma unroll
+        for (int r = 0; r < RP; ++r) upre[k][r] = (ok && r < draws) ? upre[k][r] : 0.f;
         // 64 consecutive entries lie in one half of one query
         const float m = wave_max(fabsf(qv[k]));
-        if (lane == 0 && e < NQ * kHeadDim) amax[e / kHeadDim][(e % kHeadDim) / 64] = m;
+        if (lane == 0 && ok) amax[e / kHeadDim][(e % kHeadDim) / 64] = m;
     }
     __syncthreads();
 #pragma unroll
