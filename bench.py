@@ -34,7 +34,8 @@ METRIC = "decode-attn µs/step + achieved HBM GB/s (% peak), 32k ctx, S=128, 1×
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 # the sources of the dominant kernel (prop pass 1), whose HBM counters
 # profiles/traffic.json holds
-KERNEL_SOURCES = ["santa_prop_pass1.hip", "santa_kernels.h", "santa_score.h", "santa_device.h", "santa_launch.h"]
+KERNEL_SOURCES = ["santa_prop_pass1.hip", "santa_prop_body.h", "santa_kernels.h", "santa_score.h", "santa_device.h",
+                  "santa_launch.h"]
 
 
 def kernel_source_hash():
@@ -323,6 +324,15 @@ def batch16_block(sa, BM, synth, to_device, torch, dev0, args):
 
     pms, pk = time_steps(prop_step, args.steps, args.warmup, events=True)
     pgs, _ = time_graph(prop_step, ncopy, args.steps, args.warmup)
+    zms = None
+    if not args.no_fused:
+        wsz = sa.new_workspace(dev.problem, "prop", S, dev0)
+
+        def fused_step(i):
+            sa.santa_decode_prop_fused(dev.problem, dev.q, dev.k, dev.v, S, u, out, workspace=wsz)
+
+        zms, _zk = time_steps(fused_step, args.steps, args.warmup)
+        log(f"bench: batch 16 prop in one launch {zms * 1e3:.2f} us/step")
     max_nt = (cfg.seq_len + T - 1) // T
     tb = torch.empty((BH, max_nt), dtype=torch.int32, device=dev0)
     sa.santa_decode_prop(dev.problem, dev.q, dev.k, dev.v, S, u, out, None, tb, workspace=ws)
@@ -347,6 +357,7 @@ def batch16_block(sa, BM, synth, to_device, torch, dev0, args):
                  "pass1_kernel_us": round(float(np.mean(pk)) * 1e3, 3),
                  "pass1_frac_of_peak": round(nb["pass1"] / (np.mean(pk) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                  "algorithmic_bytes_per_step": nb},
+        "single_launch_us_per_step": None if zms is None else round(zms * 1e3, 3),
         "flash": {"S": Sf, "us_per_step": round(fms * 1e3, 3),
                   "GB/s": round(fb["total"] / (fms * 1e-3) / 1e9, 1),
                   "tile_kernel_us": round(float(np.mean(fk)) * 1e3, 3)},
@@ -379,6 +390,8 @@ def main(argv=None):
                     help="skip the S2ANTA-flash leg (run where the workload has a flash budget)")
     ap.add_argument("--no-bernoulli", action="store_true",
                     help="skip prop on Bernoulli qK^T scores (contiguous bf16 and e4m3 workloads)")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip prop in one launch (santa_decode_prop_fused)")
     ap.add_argument("--no-batch16", action="store_true",
                     help="skip the secondary 32k batch-16 block (prop, flash S=2048, exact) that the "
                          "headline run adds")
@@ -521,6 +534,26 @@ def main(argv=None):
             sms, _sk = time_steps(smp_step, args.steps, args.warmup)
             log(f"bench: prop with {smp} thresholds {sms * 1e3:.2f} us/step (eager)")
             result["samplers"][smp] = {"us_per_step": round(sms * 1e3, 3)}
+
+    if not args.no_fused:
+        # S2ANTA-prop in one launch (the group's last workgroup samples), on a
+        # zeroed workspace (its arrival counters)
+        wsz = sa.new_workspace(dev.problem, "prop", S, dev0)
+
+        def fused_step(i):
+            c = i % ncopy
+            sa.santa_decode_prop_fused(dev.problem, dev.q, ks[c], vs[c], S, u, out, workspace=wsz)
+
+        zms, zk = time_steps(fused_step, args.steps, args.warmup, events=True)
+        zgs, _ = time_graph(fused_step, ncopy, args.steps, args.warmup)
+        log(f"bench: prop in one launch {zms * 1e3:.2f} us/step (graph {zgs * 1e3:.2f}), kernel {np.mean(zk) * 1e3:.2f} us")
+        result["single_launch"] = {
+            "us_per_step": round(zms * 1e3, 3), "graph_us_per_step": round(zgs * 1e3, 3),
+            "kernel_us": round(float(np.mean(zk)) * 1e3, 3),
+            "vs_two_launch": round(ms_eager / zms, 3),
+            "note": "santa_decode_prop_fused: pass 1 in every workgroup, reducer and pass 2 in each KV "
+                    "group's last-arriving workgroup (agent-scope release + arrival count per workgroup)",
+        }
 
     if cfg.S_flash and not args.no_flash:
         Sf = cfg.S_flash

@@ -103,8 +103,13 @@ typedef struct {
  * Bytes of device workspace the given variant needs for this problem and S
  * (S is ignored for SANTA_VARIANT_EXACT).  Writes *bytes; returns a status
  * (the same validation as the decode calls).  The workspace must be 256-byte
- * aligned; its contents need not be initialised.
+ * aligned.  Every variant's workspace starts with SANTA_SYNC_BYTES of arrival
+ * counters that only santa_decode_prop_fused uses: they must be zero before
+ * a workspace is first passed to it (allocate the workspace zeroed, or zero
+ * that prefix once), and every call leaves them zero; no other call reads
+ * or writes them.  The rest of the workspace need not be initialised.
  */
+#define SANTA_SYNC_BYTES (64u << 10)
 int santa_workspace_size(const santa_problem *p, int32_t variant, int32_t S, size_t *bytes);
 
 /*
@@ -130,6 +135,28 @@ int santa_decode_prop(const santa_problem *p, const void *q, const void *k, cons
                       int32_t S, const float *u, float *out, int32_t *sample_idx,
                       int32_t *tile_budget, void *workspace, size_t workspace_bytes,
                       void *stream);
+
+/*
+ * S2ANTA-prop in a single launch ("key design 2" with its global step as a
+ * per-group arrival count instead of a kernel boundary).  Every workgroup
+ * scores its tile and writes its stash and tile statistics as in
+ * santa_decode_prop, publishes them (an agent-scope release) and increments
+ * its (request, KV group)'s counter; the workgroup that completes the count
+ * runs the reducer and pass 2 of the group's heads and resets the counter.
+ * No workgroup waits for another.  Results: the same indices and budgets as
+ * santa_decode_prop (the same arithmetic); the output sums the same rows in
+ * another order (4 waves per head instead of 16), so it may differ in the
+ * last bits.
+ *   arguments    as for santa_decode_prop (systematic thresholds)
+ *   workspace    santa_workspace_size(p, SANTA_VARIANT_PROP, S) bytes whose
+ *                first SANTA_SYNC_BYTES are zero (see above); calls sharing
+ *                a workspace must not overlap in time
+ *   B * Hkv must not exceed 1024 (else SANTA_ERR_UNSUPPORTED)
+ */
+int santa_decode_prop_fused(const santa_problem *p, const void *q, const void *k, const void *v,
+                            int32_t S, const float *u, float *out, int32_t *sample_idx,
+                            int32_t *tile_budget, void *workspace, size_t workspace_bytes,
+                            void *stream);
 
 /* Threshold generators of prop ("key design 1"). */
 typedef enum {

@@ -17,6 +17,7 @@ from ._lib import SantaError, santa_problem, SANTA_F32, SANTA_BF16, SANTA_FP8_E4
 __all__ = [
     "Problem", "santa_workspace_size", "santa_decode_prop", "santa_decode_prop_sampler", "santa_decode_flash",
     "santa_decode_flash_sampler", "santa_decode_prop_bernoulli", "santa_decode_prop_static",
+    "santa_decode_prop_fused", "new_workspace",
     "exact_decode_ref", "santa_set_timing_events", "SantaError",
 ]
 
@@ -174,13 +175,19 @@ def santa_workspace_size(problem: Problem, variant: str, S: int = 0) -> int:
     return n.value
 
 
+def new_workspace(problem, variant, S=0, device="cuda"):
+    """A workspace for `variant`, allocated zeroed (the arrival counters that
+    santa_decode_prop_fused needs at zero are its first SANTA_SYNC_BYTES)."""
+    import torch
+    return torch.zeros(max(santa_workspace_size(problem, variant, S), 1), dtype=torch.uint8, device=device)
+
+
 def _workspace(fn, problem, variant, S, workspace, device):
     """(workspace tensor, its byte count): the caller's, checked, or a new one."""
     need = santa_workspace_size(problem, variant, S)
     if workspace is not None:
         return workspace, _ws_bytes(fn, workspace, need, device)
-    import torch
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    ws = new_workspace(problem, variant, S, device)
     return ws, ws.numel()
 
 
@@ -193,6 +200,19 @@ def santa_decode_prop(problem: Problem, q, k, v, S, u, out, sample_idx=None, til
                                        _ptr(sample_idx), _ptr(tile_budget), _ptr(ws), nb,
                                        _stream(stream))
     _lib._check("santa_decode_prop", st)
+    return ws
+
+
+def santa_decode_prop_fused(problem: Problem, q, k, v, S, u, out, sample_idx=None, tile_budget=None,
+                            workspace=None, stream=None):
+    """prop in one launch; a caller's workspace must come from
+    new_workspace() or otherwise start with SANTA_SYNC_BYTES of zeros."""
+    fn = "santa_decode_prop_fused"
+    _check_args(fn, problem, q, k, v, out, _sampled_extra(fn, problem, S, u, sample_idx, tile_budget, 0))
+    ws, nb = _workspace(fn, problem, "prop", S, workspace, q.device)
+    st = _lib.load().santa_decode_prop_fused(problem.ref, _ptr(q), _ptr(k), _ptr(v), S, _ptr(u), _ptr(out),
+                                             _ptr(sample_idx), _ptr(tile_budget), _ptr(ws), nb, _stream(stream))
+    _lib._check(fn, st)
     return ws
 
 

@@ -18,6 +18,7 @@ LIB_PATH = os.environ.get("SANTA_LIB") or os.path.join(HERE, "libsanta.so")
 SANTA_OK, SANTA_ERR_INVALID, SANTA_ERR_UNSUPPORTED, SANTA_ERR_WORKSPACE, SANTA_ERR_HIP = 0, -1, -2, -3, -4
 SANTA_ERR_TOO_LARGE = -5
 SANTA_STATIC_SCRATCH_BYTES = 32 << 20
+SANTA_SYNC_BYTES = 64 << 10
 SANTA_F32, SANTA_BF16, SANTA_FP8_E4M3 = 0, 1, 2
 VARIANT = {"prop": 0, "flash": 1, "exact": 2}
 SAMPLER = {"sys": 0, "strat": 1, "iid": 2}
@@ -25,6 +26,7 @@ SAMPLER = {"sys": 0, "strat": 1, "iid": 2}
 EXPORTS = [
     "santa_workspace_size", "santa_decode_prop", "santa_decode_prop_sampler", "santa_decode_flash",
     "santa_decode_flash_sampler", "santa_decode_prop_bernoulli", "exact_decode_ref", "santa_decode_prop_static",
+    "santa_decode_prop_fused",
     "santa_set_timing_events", "santa_status_string", "santa_abi_version",
 ]
 
@@ -88,6 +90,8 @@ def load():
     sampled = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     L.santa_decode_prop.argtypes = sampled
     L.santa_decode_prop.restype = C.c_int
+    L.santa_decode_prop_fused.argtypes = sampled
+    L.santa_decode_prop_fused.restype = C.c_int
     L.santa_decode_prop_sampler.argtypes = [P, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     L.santa_decode_prop_sampler.restype = C.c_int
     L.santa_decode_flash.argtypes = sampled

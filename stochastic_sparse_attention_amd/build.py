@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "libsanta.so")
 ARCH = os.environ.get("SANTA_OFFLOAD_ARCH", "gfx950")
 
 # kernel sources, each compiled once per KV storage type (-DSANTA_KV=...)
-KV_SOURCES = ["santa_prop.hip", "santa_prop_pass1.hip", "santa_flash.hip", "santa_exact.hip"]
+KV_SOURCES = ["santa_prop.hip", "santa_prop_pass1.hip", "santa_prop_fused.hip", "santa_flash.hip", "santa_exact.hip"]
 KV_TYPES = {"bf16": "uint16_t", "fp8": "uint8_t", "f32": "float"}
 # sources built once: Bernoulli scoring (bf16 and e4m3 in one unit) and the
 # allocation-free prop entry point (its static device workspace)
@@ -21,7 +21,7 @@ ONE_TYPE_SOURCES = ["santa_bernoulli.hip", "santa_static.hip"]
 # host sources, compiled once
 HOST_SOURCES = ["santa_api.cpp", "santa_dispatch.cpp"]
 SOURCES = KV_SOURCES + ONE_TYPE_SOURCES + HOST_SOURCES
-HEADERS = ["santa_device.h", "santa_score.h", "santa_launch.h", "santa_kernels.h"]
+HEADERS = ["santa_device.h", "santa_score.h", "santa_launch.h", "santa_kernels.h", "santa_prop_body.h"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -87,6 +87,9 @@ size_t carve(const santa_problem *p, int variant, const Derived &d, char *base, 
         return ptr;
     };
     santa::Workspace w{};
+    // every variant's layout starts with the single-launch prop's counters,
+    // so that no other call ever writes over them
+    w.sync = take(santa::kSyncBytes);
     if (variant == SANTA_VARIANT_PROP) {
         // every tile in full, also the short last one (aligned wide stores,
         // and whole-tile reads in pass 2)
@@ -184,6 +187,24 @@ int santa_decode_prop(const santa_problem *p, const void *q, const void *k, cons
                        workspace, workspace_bytes, stream);
 }
 
+int santa_decode_prop_fused(const santa_problem *p, const void *q, const void *k, const void *v, int32_t S,
+                            const float *u, float *out, int32_t *sample_idx, int32_t *tile_budget,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    Derived d;
+    int st = validate(p, SANTA_VARIANT_PROP, S, &d);
+    if (st != SANTA_OK) return st;
+    if ((long)p->batch * p->num_kv_heads > santa::kMaxSyncGroups) return SANTA_ERR_UNSUPPORTED;
+    if (p->batch == 0) return SANTA_OK;
+    if (!q || !k || !v || !u || !out) return SANTA_ERR_INVALID;
+    santa::Workspace ws;
+    st = check_workspace(p, SANTA_VARIANT_PROP, d, workspace, workspace_bytes, &ws);
+    if (st != SANTA_OK) return st;
+    santa::LaunchArgs a = make_args(p, d, q, k, v, S, u, out, sample_idx, tile_budget, ws, stream);
+    a.sampler = SANTA_SAMPLER_SYS;
+    const santa::TimingHook hook{g_ev_begin, g_ev_end};
+    return santa::launch_prop_fused(a, hook) == hipSuccess ? SANTA_OK : SANTA_ERR_HIP;
+}
+
 int santa_decode_prop_sampler(const santa_problem *p, const void *q, const void *k, const void *v,
                               int32_t S, int32_t sampler, const float *u, float *out,
                               int32_t *sample_idx, int32_t *tile_budget, void *workspace,
@@ -276,6 +297,6 @@ const char *santa_status_string(int status) {
     }
 }
 
-int santa_abi_version(void) { return 5; }
+int santa_abi_version(void) { return 6; }
 
 }  // extern "C"

@@ -28,6 +28,7 @@ hipError_t launch_prop_bernoulli(const LaunchArgs &a, const TimingHook &hook) {
     return launch_sample(a, hook);
 }
 
+hipError_t launch_prop_fused(const LaunchArgs &a, const TimingHook &hook) { SANTA_KV_SWITCH(launch_prop_fused_kv) }
 hipError_t launch_flash(const LaunchArgs &a, const TimingHook &hook) { SANTA_KV_SWITCH(launch_flash_kv) }
 hipError_t launch_exact(const LaunchArgs &a, const TimingHook &hook) { SANTA_KV_SWITCH(launch_exact_kv) }
 

@@ -24,8 +24,16 @@ __host__ __device__ inline int threshold_slots(int S, int sampler) {
     return p;
 }
 
+// Arrival counters of the single-launch prop: the first kSyncBytes of every
+// workspace, one counter per (request, KV group) every kSyncStride words;
+// zero before the first call, and every call leaves them zero.
+constexpr int kSyncStride = 16;                        // 64 bytes apart
+constexpr size_t kSyncBytes = 64 * 1024;
+constexpr int kMaxSyncGroups = (int)(kSyncBytes / (kSyncStride * 4));
+
 // Carved workspace regions (device pointers; unused ones are null).
 struct Workspace {
+    void *sync;       // every variant: [kMaxSyncGroups * kSyncStride] uint32 (the single-launch prop's counters)
     void *stash;      // prop: [B, Hq, max_nt * T] fp32
     void *stats;      // prop: [B, Hq, max_nt] float2
     void *part_m;     // flash/exact: [B, Hq, max_nt] fp32
@@ -72,6 +80,9 @@ hipError_t launch_exact(const LaunchArgs &a, const TimingHook &hook);
 // prop with Bernoulli qK^T scores (bf16, contiguous): its pass 1, then the
 // same reducer + pass 2 as launch_prop
 hipError_t launch_prop_bernoulli(const LaunchArgs &a, const TimingHook &hook);
+// prop in one launch (pass 1, then the reducer and pass 2 in each group's
+// last workgroup)
+hipError_t launch_prop_fused(const LaunchArgs &a, const TimingHook &hook);
 hipError_t launch_bernoulli_pass1(const LaunchArgs &a, const TimingHook &hook);
 
 // The launchers per KV storage type (uint16_t bf16, uint8_t e4m3, float).
@@ -81,5 +92,6 @@ template <typename KV> hipError_t launch_prop_pass1_kv(const LaunchArgs &a, cons
 template <typename KV> hipError_t launch_prop_sample_kv(const LaunchArgs &a, const TimingHook &hook);
 template <typename KV> hipError_t launch_flash_kv(const LaunchArgs &a, const TimingHook &hook);
 template <typename KV> hipError_t launch_exact_kv(const LaunchArgs &a, const TimingHook &hook);
+template <typename KV> hipError_t launch_prop_fused_kv(const LaunchArgs &a, const TimingHook &hook);
 
 }  // namespace santa

@@ -28,7 +28,7 @@ def _torch():
     return torch
 
 
-def run_prop(dev, S, T=None, sampler="sys", uniforms=None):
+def run_prop(dev, S, T=None, sampler="sys", uniforms=None, fused=False, workspace=None):
     torch = _torch()
     c = dev.inp.cfg
     BH = c.batch * c.num_q_heads
@@ -40,8 +40,10 @@ def run_prop(dev, S, T=None, sampler="sys", uniforms=None):
     import stochastic_sparse_attention_amd as sa
     if sampler == "sys":
         uu = dev.u(S) if uniforms is None else torch.from_numpy(uniforms).to(dev.q.device)
-        sa.santa_decode_prop(dev.problem, dev.q, dev.k, dev.v, S, uu, out, idx, tb)
+        call = sa.santa_decode_prop_fused if fused else sa.santa_decode_prop
+        call(dev.problem, dev.q, dev.k, dev.v, S, uu, out, idx, tb, workspace=workspace)
     else:
+        assert not fused
         uu = dev.uniforms(S) if uniforms is None else torch.from_numpy(uniforms).to(dev.q.device)
         sa.santa_decode_prop_sampler(dev.problem, dev.q, dev.k, dev.v, S, sampler, uu, out, idx, tb)
     torch.cuda.synchronize()
@@ -141,7 +143,8 @@ def index_report(gpu_idx, ora_idx, delta, cells_of=None):
             "max_exempt_cell_distance": worst}
 
 
-def check_prop(dev, S, repeat=True, sampler="sys", uniforms=None, oracle_uniforms=None):
+def check_prop(dev, S, repeat=True, sampler="sys", uniforms=None, oracle_uniforms=None, fused=False,
+               workspace=None):
     """Run prop on the GPU (systematic, stratified or i.i.d. thresholds) and
     hold it to the bar; returns a report dict.  `uniforms` replaces the
     seeded offsets [B*Hq] (systematic) or uniforms [B*Hq, S] (list
@@ -150,7 +153,7 @@ def check_prop(dev, S, repeat=True, sampler="sys", uniforms=None, oracle_uniform
     inp = dev.inp
     c = inp.cfg
     T = dev.problem.s.tile_len
-    out, idx, tb = run_prop(dev, S, sampler=sampler, uniforms=uniforms)
+    out, idx, tb = run_prop(dev, S, sampler=sampler, uniforms=uniforms, fused=fused, workspace=workspace)
     prob = oracle_problem(dev)
     ou = oracle_uniforms if oracle_uniforms is not None else uniforms
     if sampler == "sys":
@@ -185,7 +188,7 @@ def check_prop(dev, S, repeat=True, sampler="sys", uniforms=None, oracle_uniform
     rep["max_abs_vs_replay"] = err
     rep["max_abs_vs_oracle_estimate"] = float(np.max(np.abs(out - r["out"])))
     if repeat:
-        out2, idx2, tb2 = run_prop(dev, S, sampler=sampler, uniforms=uniforms)
+        out2, idx2, tb2 = run_prop(dev, S, sampler=sampler, uniforms=uniforms, fused=fused, workspace=workspace)
         assert np.array_equal(idx, idx2) and np.array_equal(tb, tb2)
         assert np.array_equal(out.view(np.uint32), out2.view(np.uint32))
     return rep

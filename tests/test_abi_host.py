@@ -67,11 +67,12 @@ def test_workspace_sizes_follow_layout(lib):
     st, n = _wsize(lib, p, PROP, 128)
     assert st == OK
     BH, nt = 32, 128
+    sync = _lib.SANTA_SYNC_BYTES                           # every variant starts with the counters
     stash = BH * 32768 * 4
     stats = BH * nt * 8
-    assert n == stash + stats                              # both 256-byte multiples
+    assert n == sync + stash + stats                       # all 256-byte multiples
     st, n = _wsize(lib, p, EXACT, 0)
-    assert st == OK and n == 2 * BH * nt * 4 + BH * nt * 128 * 4
+    assert st == OK and n == sync + 2 * BH * nt * 4 + BH * nt * 128 * 4
     st, n2 = _wsize(lib, p, FLASH, 2048)
     assert st == OK and n2 == n
     # stash rows are padded to a multiple of the tile length

@@ -532,11 +532,70 @@ def test_bernoulli_prop_full_size(gpu, cid):
              parity.check_prop_bernoulli(dev, cfg.S, draws, gm, repeat=cid == 2))
 
 
+# ------------------------------------------------- single-launch prop
+def _fused_vs_two_launch(dev, S, workspace=None):
+    """The single-launch prop against the oracle (the parity bar) and against
+    the two-launch prop: the same indices and budgets, outputs equal to
+    rounding of the summation order."""
+    import parity
+    rep = parity.check_prop(dev, S, fused=True, workspace=workspace)
+    o1, i1, t1 = parity.run_prop(dev, S)
+    o2, i2, t2 = parity.run_prop(dev, S, fused=True, workspace=workspace)
+    assert np.array_equal(i1, i2) and np.array_equal(t1, t2)
+    rep["max_abs_vs_two_launch"] = float(np.max(np.abs(o1 - o2))) if o1.size else 0.0
+    assert rep["max_abs_vs_two_launch"] <= 1e-5
+    return rep
+
+
+@pytest.mark.parametrize("T", [64, 256, 1024])
+def test_fused_prop_tiles(gpu, T):
+    cfg = synth.small_config(2, batch=2, seq_len=4000)
+    _say("fused T", T, _fused_vs_two_launch(_dev(cfg, 61, gpu, tile_len=T), 128))
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (16, 2)])
+def test_fused_prop_groups(gpu, hq, hkv):
+    cfg = synth.small_config(2, batch=2, seq_len=3000, num_q_heads=hq, num_kv_heads=hkv)
+    _say("fused G", hq // hkv, _fused_vs_two_launch(_dev(cfg, 62, gpu), 64))
+
+
+def test_fused_prop_paged_ragged_empty(gpu):
+    """Paged KV, mixed lengths and an empty request (which counts no tile:
+    its tile-0 workgroup writes the empty results)."""
+    from stochastic_sparse_attention_amd.device_io import to_device
+    cfg = synth.small_config(5, batch=5, seq_len=3000, min_seq_len=100)
+    inp = synth.make_inputs(cfg, 63)
+    seq = inp.seq_lens.copy()
+    seq[1] = 0
+    _say("fused paged ragged empty", _fused_vs_two_launch(to_device(inp, gpu, seq_lens=seq), 128))
+
+
+def test_fused_prop_full_size(gpu):
+    cfg = synth.CONFIGS[2]
+    _say("fused full size", _fused_vs_two_launch(_dev(cfg, cfg.cid, gpu), cfg.S))
+
+
+def test_fused_prop_counters_reset(gpu):
+    """The arrival counters return to zero after every call: one workspace
+    serves repeated calls, and a call on another problem in between (whose
+    counters overlap the first problem's), each result still at the bar."""
+    import stochastic_sparse_attention_amd as sa
+    import torch
+    big = _dev(synth.small_config(2, batch=4, seq_len=6000), 64, gpu)
+    small = _dev(synth.small_config(2, batch=1, seq_len=1500, num_q_heads=8, num_kv_heads=2), 65, gpu, tile_len=64)
+    ws = sa.new_workspace(big.problem, "prop", 128, gpu)
+    for rep in range(2):
+        _say("fused reuse big", rep, _fused_vs_two_launch(big, 128, workspace=ws))
+        _say("fused reuse small", rep, _fused_vs_two_launch(small, 32, workspace=ws))
+    torch.cuda.synchronize()
+    assert int(ws[:sa._lib.SANTA_SYNC_BYTES].count_nonzero()) == 0
+
+
 # ------------------------------------------------- HIP graph replay
 def test_graph_replays_match_eager(gpu):
-    """prop (all three threshold generators, and on Bernoulli scores with the
-    mean group query), flash (systematic and stratified) and exact decode
-    captured in one HIP graph: every replay,
+    """prop (all three threshold generators, on Bernoulli scores with the
+    mean group query, and in one launch), flash (systematic and stratified)
+    and exact decode captured in one HIP graph: every replay,
     with eager work and synchronisations in between, gives results bitwise
     equal to the eager calls."""
     import torch
@@ -552,7 +611,8 @@ def test_graph_replays_match_eager(gpu):
     UF, uuf = dev.u(SF), dev.uniforms(SF)
     wsf = torch.empty(sa.santa_workspace_size(dev.problem, "flash", SF), dtype=torch.uint8, device=gpu)
     outs = {k: torch.empty((BH, 128), dtype=torch.float32, device=gpu)
-            for k in ("sys", "strat", "iid", "exact", "flash", "flash_strat", "bernoulli")}
+            for k in ("sys", "strat", "iid", "exact", "flash", "flash_strat", "bernoulli", "fused")}
+    wsz = sa.new_workspace(dev.problem, "prop", S, gpu)
     kf, ub = dev.k_features(), dev.bernoulli_uniforms(4, True)
     fr = torch.empty(cfg.batch * cfg.num_kv_heads, dtype=torch.int32, device=gpu)
     idx = torch.empty((BH, S), dtype=torch.int32, device=gpu)
@@ -568,6 +628,7 @@ def test_graph_replays_match_eager(gpu):
                                       workspace=wsf)
         sa.santa_decode_prop_bernoulli(dev.problem, dev.q, kf, dev.v, S, U, 4, 1, ub, outs["bernoulli"],
                                        features_read=fr, workspace=ws)
+        sa.santa_decode_prop_fused(dev.problem, dev.q, dev.k, dev.v, S, U, outs["fused"], workspace=wsz)
 
     step()
     torch.cuda.synchronize()
