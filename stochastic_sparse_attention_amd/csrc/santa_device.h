@@ -172,6 +172,9 @@ __device__ __forceinline__ double dpp_d(double ident, double v) {
 
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
 constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+// whole-wave shift by one lane (lane l reads lane l-1; lane 0 keeps the
+// identity): a DPP control the GFX9-family parts, gfx950 among them, keep
+constexpr int kWaveShr1 = 0x138;
 
 __device__ __forceinline__ float wave_incl_scan(float v, int /*lane*/) {
     v += dpp_f<kRowShr1, 0xF>(0.f, v);

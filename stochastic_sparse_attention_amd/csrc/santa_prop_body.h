@@ -133,6 +133,7 @@ struct VisitRec {
 };
 
 constexpr int kRegisterTiles = 256;  // up to this many tiles the reducer keeps them in registers
+constexpr int kStepSlots = 16;       // stepping lanes a wave stages in LDS at a time (systematic pass 2)
 constexpr int kGatherRounds = 4;     // V rows per lane slot in flight together in the gather
 
 // EPL consecutive floats from a 16-byte aligned address (EPL = T/64)
@@ -202,16 +203,21 @@ struct ListCount {
 constexpr int kStatRegs = kRegisterTiles / 64;   // tiles per reducer lane held in registers
 
 // the reducer lane's tile statistics (m_t, Z_t) for the register reducer,
-// (-inf, 0) past the lane's tiles; issued early so that their latency
-// overlaps other work
+// (-inf, 0) past the lane's tiles (nt >= 1).  Every load is issued
+// unconditionally, from a clamped index, and masked afterwards: under a
+// per-lane condition each load became a branch, and the last one waited
+// for all of them on the spot
 __device__ __forceinline__ void load_lane_stats(const float2 *__restrict__ stp, int nt, int lane,
                                                 float2 (&st)[kStatRegs]) {
     const int CH = (nt + 63) / 64;
     const int tb = lane * CH;
+    float2 raw[kStatRegs];
+#pragma unroll
+    for (int i = 0; i < kStatRegs; ++i) raw[i] = stp[min(tb + i, nt - 1)];
 #pragma unroll
     for (int i = 0; i < kStatRegs; ++i) {
         const bool ok = i < CH && tb + i < nt;
-        st[i] = ok ? stp[tb + i] : make_float2(-INFINITY, 0.f);
+        st[i] = ok ? raw[i] : make_float2(-INFINITY, 0.f);
     }
 }
 
@@ -481,6 +487,11 @@ __device__ __forceinline__ void sample_head(
     __shared__ int nvis_sh;
     __shared__ int wrow[NW][kWave];        // per-wave compacted marker rows
     __shared__ float wmul[NW][kWave];      // and their multiplicities
+    // per-wave slots of the lanes whose count steps (systematic thresholds):
+    // their in-lane prefixes, (b_lane, a, hi, prev) and first token row
+    __shared__ __align__(16) float stepP[NW][kStepSlots][16];
+    __shared__ float4 stepM[NW][kStepSlots];
+    __shared__ int stepRow[NW][kStepSlots];
 
     const int bh = b * num_q_heads + g * G + hl;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -495,11 +506,16 @@ __device__ __forceinline__ void sample_head(
         if (tid < kHeadDim) out[(size_t)bh * kHeadDim + tid] = 0.f;
         return;
     }
-    // the reducer's tile statistics, issued first so that their latency
-    // overlaps the threshold loads below
+    // the reducer's inputs, issued first and together: the systematic
+    // offset and the tile statistics (their latency overlaps the threshold
+    // loads below)
     const float2 *stp = stats + (size_t)bh * max_nt;
     float2 st[kStatRegs];
-    if (w == 0 && nt <= kRegisterTiles) load_lane_stats(stp, nt, lane, st);
+    float u_sys = 0.f;
+    if (w == 0) {
+        if constexpr (!LIST) u_sys = u[bh];
+        if (nt <= kRegisterTiles) load_lane_stats(stp, nt, lane, st);
+    }
 
     // ---------------- thresholds of the stratified and i.i.d. generators:
     // (m + u_m)/S, or the uniforms sorted, in fp64 (uniforms outside [0,1)
@@ -591,7 +607,7 @@ __device__ __forceinline__ void sample_head(
         int *budget = tile_budget ? tile_budget + (size_t)bh * max_nt : nullptr;
         const ReducerLds R{tstat, tf, tC, tcn};
         if constexpr (!LIST)
-            reduce_head(stp, st, nt, lane, SysCount{clamp_offset(u[bh], S), S}, scale, kcap, vis, budget, max_nt, nvis_sh, R);
+            reduce_head(stp, st, nt, lane, SysCount{clamp_offset(u_sys, S), S}, scale, kcap, vis, budget, max_nt, nvis_sh, R);
         else
             reduce_head(stp, st, nt, lane, ListCount{thr, S, sampler == kSamplerStrat}, scale, kcap, vis, budget,
                         max_nt, nvis_sh, R);
@@ -668,7 +684,7 @@ __device__ __forceinline__ void sample_head(
             e[qq] = run;                                   // in-lane inclusive prefix
         }
         const float gincl = group_incl_scan<LPT>(run);
-        float excl = __shfl_up(gincl, 1);                  // sum of the earlier lanes of the group
+        float excl = dpp_f<kWaveShr1, 0xF>(0.f, gincl);   // sum of the earlier lanes of the group
         if (gl == 0) excl = 0.f;
         // x_j = P_j a + b for the lane's tokens: e_j a + (excl a + b), monotone
         // in the lane; across lanes a running max keeps the counts monotone
@@ -682,59 +698,91 @@ __device__ __forceinline__ void sample_head(
         const int yl = list ? count_in_range(lcnt, (double)fmaf(e[EPL2 - 1], rec.a, bl), lo, hi)
                             : max((int)fminf(ceilf(fmaf(e[EPL2 - 1], rec.a, bl)), fhi), lo);
         const int gmax = group_incl_max<LPT>(yl);
-        int prev = __shfl_up(gmax, 1);                     // count reached by the earlier lanes
+        int prev = dpp_i<kWaveShr1, 0xF>(0, gmax);        // count reached by the earlier lanes
         if (gl == 0) prev = lo;
-        if (active && yl > prev) {                         // thresholds prev .. yl-1 fall on this lane
-            int yp = prev;
-            // a step can fall on a token of zero weight only through fp32
-            // rounding across lanes (a threshold within ~1e-7 of that
-            // token's CDF position); past the sequence end such a token is
-            // replaced by the last one, so every row read is inside the
-            // request
-            if constexpr (!LIST) {
+        // Thresholds prev .. yl-1 fall on the lane's tokens.  A step can fall
+        // on a token of zero weight only through fp32 rounding across lanes
+        // (a threshold within ~1e-7 of that token's CDF position); past the
+        // sequence end such a token is replaced by the last one, so every
+        // row read is inside the request.
+        if constexpr (!LIST) {
+            // Systematic: y_q = min(ceil(P_q a + b), hi) is nondecreasing
+            // along the lane (P_q is a prefix of nonnegative weights, a >= 0,
+            // and fma, ceil and min are monotone), so token q steps exactly
+            // when y_q > z_q = max(prev, y_{q-1}) (z_0 = prev), and its
+            // marker sits at z_q with multiplicity y_q - z_q.  The lanes
+            // that step (a few per tile) put their prefixes into the wave's
+            // LDS slots; the wave then evaluates SPP such lanes per pass, one
+            // token per thread, instead of every lane walking its EPL2
+            // tokens.
+            constexpr int SPP = kWave / EPL2;
+            const bool steps = active && yl > prev;
+            const unsigned long long smask = __ballot(steps);
+            const int nstep = __popcll(smask);
+            const int rank = __builtin_amdgcn_mbcnt_hi((unsigned)(smask >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((unsigned)smask, 0u));
+            const int q = lane % EPL2;
+            for (int base = 0; base < nstep; base += kStepSlots) {
+                const int sl = rank - base;
+                if (steps && sl >= 0 && sl < kStepSlots) {
 #pragma unroll
-                for (int qq = 0; qq < EPL2; ++qq) {
-                    const int y = (int)fminf(ceilf(fmaf(e[qq], rec.a, bl)), fhi);
-                    if (y > yp) {
-                        jsel[yp] = min(start + gl * EPL2 + qq, n - 1);
-                        jmul[yp] = y - yp;
-                        yp = y;
+                    for (int q4 = 0; q4 < EPL2; q4 += 4)
+                        *reinterpret_cast<float4 *>(&stepP[w][sl][q4]) = make_float4(e[q4], e[q4 + 1], e[q4 + 2], e[q4 + 3]);
+                    stepM[w][sl] = make_float4(bl, rec.a, fhi, __int_as_float(prev));
+                    stepRow[w][sl] = start + gl * EPL2;
+                }
+                wave_sync_lds();
+                const int cnt = min(nstep - base, kStepSlots);
+                for (int p0 = 0; p0 < cnt; p0 += SPP) {
+                    const int s2 = p0 + lane / EPL2;
+                    const int sc = s2 < cnt ? s2 : 0;
+                    const float4 m = stepM[w][sc];
+                    const int y = (int)fminf(ceilf(fmaf(stepP[w][sc][q], m.y, m.x)), m.z);
+                    const int pv = __float_as_int(m.w);
+                    const int ym1 = dpp_i<kRowShr1, 0xF>(0, y);  // y_{q-1}: same slot for q >= 1
+                    const int z = q == 0 ? pv : max(pv, ym1);
+                    if (s2 < cnt && y > z) {
+                        jsel[z] = min(stepRow[w][sc] + q, n - 1);
+                        jmul[z] = y - z;
                     }
                 }
-            } else {
-                // merge of the lane's tokens with its thresholds.  The next
-                // threshold is kept in a register as the largest float at
-                // or below it: for a float F, thr < F exactly when that
-                // float is < F, so the test is the fp64 one.  A token past
-                // it reaches clamp(#{thr < F}, yp + 1, yl): one closed-form
-                // count (stratified) or one bisection (i.i.d.) per token that
-                // holds thresholds, however many it holds.
-                float nxt = float_at_or_below(thr[yp]);     // yp < yl <= S here
+                wave_sync_lds();
+            }
+        } else if (active && yl > prev) {
+            // stratified / i.i.d.: merge of the lane's tokens with its
+            // thresholds.  The next threshold is kept in a register as the
+            // largest float at or below it: for a float F, thr < F exactly
+            // when that float is < F, so the test is the fp64 one.  A token
+            // past it reaches clamp(#{thr < F}, yp + 1, yl): one closed-form
+            // count (stratified) or one bisection (i.i.d.) per token that
+            // holds thresholds, however many it holds.
+            int yp = prev;
+            float nxt = float_at_or_below(thr[yp]);         // yp < yl <= S here
 #pragma unroll
-                for (int qq = 0; qq < EPL2; ++qq) {
-                    const float Fq = fmaf(e[qq], rec.a, bl);
-                    if (nxt < Fq) {
-                        const int y = count_in_range(lcnt, (double)Fq, yp + 1, yl);
-                        jsel[yp] = min(start + gl * EPL2 + qq, n - 1);
-                        jmul[yp] = y - yp;
-                        yp = y;
-                        nxt = yp < yl ? float_at_or_below(thr[yp]) : INFINITY;
-                    }
+            for (int qq = 0; qq < EPL2; ++qq) {
+                const float Fq = fmaf(e[qq], rec.a, bl);
+                if (nxt < Fq) {
+                    const int y = count_in_range(lcnt, (double)Fq, yp + 1, yl);
+                    jsel[yp] = min(start + gl * EPL2 + qq, n - 1);
+                    jmul[yp] = y - yp;
+                    yp = y;
+                    nxt = yp < yl ? float_at_or_below(thr[yp]) : INFINITY;
                 }
             }
         }
-        const int yend = __builtin_amdgcn_ds_bpermute(4 * group_last_lane<LPT>(lane), gmax);
-        if (active && yend < hi) {
-            // rare: the fp32 tile total is short of the tile's last threshold;
-            // thresholds yend .. hi-1 go to the last token whose weight moved P
+        // rare: the fp32 tile total is short of the tile's last threshold
+        // (the count at the group's last lane, gmax there, is below hi);
+        // thresholds gmax .. hi-1 go to the last token whose weight moved P
+        const bool short_tile = active && gl == LPT - 1 && gmax < hi;
+        if (__ballot(short_tile)) {
             int lz = -1;
 #pragma unroll
             for (int qq = 0; qq < EPL2; ++qq)
                 if (e[qq] > (qq ? e[qq - 1] : 0.f)) lz = gl * EPL2 + qq;
             lz = group_incl_max<LPT>(lz);
-            if (gl == LPT - 1) {
-                jsel[yend] = start + max(lz, 0);
-                jmul[yend] = hi - yend;
+            if (short_tile) {
+                jsel[gmax] = start + max(lz, 0);
+                jmul[gmax] = hi - gmax;
             }
         }
         // the wave's threshold range [m0, m1): from its first tile's first
