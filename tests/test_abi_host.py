@@ -201,3 +201,18 @@ def test_bernoulli_entry_validates_before_launch(lib):
     assert _bern(lib, p, ws_bytes=16) == WORKSPACE
     assert _bern(lib, p, S=5000) == UNSUPPORTED
     assert _bern(lib, _problem(batch=0)) == OK
+
+
+def _prop_fused(lib, p, S=128, ws_bytes=1 << 30):
+    return lib.santa_decode_prop_fused(C.byref(p), DUMMY, DUMMY, DUMMY, S, DUMMY, DUMMY, None, None, DUMMY,
+                                       ws_bytes, None)
+
+
+def test_single_launch_prop_limits(lib):
+    """The single-launch prop needs one arrival counter per (request, KV
+    group) in the workspace's SANTA_SYNC_BYTES (64 bytes apart); beyond that
+    it returns SANTA_ERR_UNSUPPORTED before any launch."""
+    groups = _lib.SANTA_SYNC_BYTES // 64
+    assert _prop_fused(lib, _problem(batch=groups // 8 + 1)) == UNSUPPORTED      # 8 KV heads per request
+    assert _prop_fused(lib, _problem(batch=groups // 8), ws_bytes=16) == WORKSPACE
+    assert _prop_fused(lib, _problem(batch=0)) == OK
