@@ -245,9 +245,6 @@ __device__ __forceinline__ int group_incl_max(int v) {
     if (LPT >= 64) v = max(v, dpp_i<kRowBcast31, 0xC>(INT_MIN, v));
     return v;
 }
-// value of the lane LPT-1 of this lane's group (the group's inclusive total)
-template <int LPT>
-__device__ __forceinline__ int group_last_lane(int lane) { return (lane | (LPT - 1)); }
 
 // wave-wide maximum, returned to every lane (lane 63 of the scan holds it)
 __device__ __forceinline__ float wave_max(float v) {
@@ -257,11 +254,6 @@ __device__ __forceinline__ int wave_max(int v) {
     return __builtin_amdgcn_readlane(wave_incl_max_scan(v, 0), 63);
 }
 
-// value of lane l-1 (lane 0 gets `first`)
-__device__ __forceinline__ float wave_shift_up(float v, float first) {
-    float u = __shfl_up(v, 1);
-    return (threadIdx.x & 63) ? u : first;
-}
 
 __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

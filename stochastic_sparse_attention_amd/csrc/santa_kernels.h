@@ -39,17 +39,6 @@ __device__ __forceinline__ V block_incl_sum(V v, V *sh) {
     return x + off;
 }
 
-__device__ __forceinline__ int block_incl_max(int v, int *sh) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int x = wave_incl_max_scan(v, lane);
-    if (lane == 63) sh[w] = x;
-    __syncthreads();
-    int off = x;
-    for (int i = 0; i < w; ++i) off = max(off, sh[i]);
-    __syncthreads();
-    return off;
-}
-
 __device__ __forceinline__ float block_max(float v, float *sh) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     v = wave_max(v);
@@ -59,58 +48,6 @@ __device__ __forceinline__ float block_max(float v, float *sh) {
     for (int i = 1; i < (int)(blockDim.x >> 6); ++i) m = fmaxf(m, sh[i]);
     __syncthreads();
     return m;
-}
-
-// Block scan returning the inclusive and exclusive prefixes and the total
-// (fixed order; excl of thread t equals incl of thread t-1 bitwise, since
-// both are formed from the same operands in the same order).
-template <typename V>
-struct ScanOut {
-    V incl, excl, total;
-};
-
-struct OpAdd {
-    template <typename V> __device__ __forceinline__ V operator()(V a, V b) const { return a + b; }
-};
-struct OpMax {
-    template <typename V> __device__ __forceinline__ V operator()(V a, V b) const { return a > b ? a : b; }
-};
-
-__device__ __forceinline__ double wave_scan_op(double v, OpAdd) { return wave_incl_scan(v, 0); }
-__device__ __forceinline__ int wave_scan_op(int v, OpAdd) { return wave_incl_scan(v, 0); }
-__device__ __forceinline__ int wave_scan_op(int v, OpMax) { return wave_incl_max_scan(v, 0); }
-
-template <typename V, typename Op>
-__device__ __forceinline__ ScanOut<V> block_scan(V v, V ident, V *sh, Op op) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int nw = (int)(blockDim.x >> 6);
-    const V x = wave_scan_op(v, op);
-    const V xe = __shfl_up(x, 1);
-    if (lane == 63) sh[w] = x;
-    __syncthreads();
-    V off = ident, total = ident;
-    for (int i = 0; i < nw; ++i) {
-        if (i == w) off = total;
-        total = (i == 0) ? sh[0] : op(total, sh[i]);
-    }
-    __syncthreads();
-    ScanOut<V> r;
-    r.incl = (w == 0) ? x : op(off, x);
-    r.excl = (lane == 0) ? off : ((w == 0) ? xe : op(off, xe));
-    r.total = total;
-    return r;
-}
-
-// value held by thread tid-1 (thread 0 gets `first`)
-template <typename V>
-__device__ __forceinline__ V block_shift_up(V v, V first, V *sh) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    V up = __shfl_up(v, 1);
-    if (lane == 63) sh[w] = v;
-    __syncthreads();
-    if (lane == 0) up = (w == 0) ? first : sh[w - 1];
-    __syncthreads();
-    return up;
 }
 
 // exp-weight e = exp(scale (x - m)) of an unscaled score x, tile max m
