@@ -27,18 +27,19 @@ struct KVLayout {
     int max_pages;
 };
 
-// Element offset of the first element of a 16-row block starting at row j0
-// (j0 % 16 == 0); rows j0..j0+15 are contiguous in both layouts.
-__device__ __forceinline__ size_t block16_offset(const KVLayout &L, int b, int g, int j0) {
-    if (L.page_size == 0)
-        return (((size_t)b * L.num_kv_heads + g) * L.max_seq_len + j0) * kHeadDim;
-    int page = L.page_table[(size_t)b * L.max_pages + j0 / L.page_size];
-    return (((size_t)page * L.num_kv_heads + g) * L.page_size + (j0 % L.page_size)) * kHeadDim;
-}
-
+// Element offset of row j of request b / KV head g.  PAGED (the layout of
+// the kernel's instantiation, page_size != 0): row j % page_size of page
+// page_table[b][j / page_size]; else the contiguous [B, Hkv, max_seq_len, d]
+// cache.  A compile-time choice, so that a kernel carries only its own
+// layout's address code.
+template <bool PAGED>
 __device__ __forceinline__ size_t row_offset(const KVLayout &L, int b, int g, int j) {
-    int j0 = j & ~15;
-    return block16_offset(L, b, g, j0) + (size_t)(j - j0) * kHeadDim;
+    if constexpr (PAGED) {
+        const int page = L.page_table[(size_t)b * L.max_pages + j / L.page_size];
+        return (((size_t)page * L.num_kv_heads + g) * L.page_size + (j % L.page_size)) * kHeadDim;
+    } else {
+        return (((size_t)b * L.num_kv_heads + g) * L.max_seq_len + j) * kHeadDim;
+    }
 }
 
 __device__ __forceinline__ int seq_len_of(const int *seq_lens, int max_seq_len, int b) {

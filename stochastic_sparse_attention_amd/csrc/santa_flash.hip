@@ -264,7 +264,7 @@ __global__ __launch_bounds__(kBlock) void flash_tile_kernel(
 #pragma unroll 4
         for (int m = slot; m < Sf; m += 4) {
             float xv[8];
-            load_v8<KV>(v + row_offset(L, b, g, sel[m]) + 8 * chunk, xv);
+            load_v8<KV>(v + row_offset<PAGED>(L, b, g, sel[m]) + 8 * chunk, xv);
 #pragma unroll
             for (int ee = 0; ee < 8; ++ee) acc[ee] += xv[ee];
         }

@@ -620,6 +620,7 @@ __device__ __forceinline__ void sample_head(
     constexpr int LPT = T >= 1024 ? 64 : (T >= 512 ? 32 : 16);
     constexpr int TPW = 64 / LPT;
     constexpr int EPL2 = T / LPT;
+    static_assert(EPL2 <= 32, "a lane's tokens fit one 32-bit mask");
     const int sub = lane / LPT, gl = lane % LPT;          // tile slot in the wave, lane in group
     const int slot = lane >> 4, chunk = lane & 15;        // gather: row slot, 8-element chunk
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // V sums of the wave's 4 row slots
@@ -655,7 +656,7 @@ __device__ __forceinline__ void sample_head(
                 Raw8<KV> raw[kGatherRounds];
 #pragma unroll
                 for (int u = 0; u < kGatherRounds; ++u)
-                    raw[u] = load_raw8<KV>(v + row_offset(L, b, g, rows[u]) + 8 * chunk);
+                    raw[u] = load_raw8<KV>(v + row_offset<PAGED>(L, b, g, rows[u]) + 8 * chunk);
 #pragma unroll
                 for (int u = 0; u < kGatherRounds; ++u) {
                     float xv[8];
@@ -775,10 +776,13 @@ __device__ __forceinline__ void sample_head(
         // thresholds gmax .. hi-1 go to the last token whose weight moved P
         const bool short_tile = active && gl == LPT - 1 && gmax < hi;
         if (__ballot(short_tile)) {
-            int lz = -1;
+            // the lane's tokens that moved P, as bits: one
+            // register, where per-token candidate indices were hoisted out
+            // of the tile loop by the compiler and spilled
+            unsigned moved = 0;
 #pragma unroll
-            for (int qq = 0; qq < EPL2; ++qq)
-                if (e[qq] > (qq ? e[qq - 1] : 0.f)) lz = gl * EPL2 + qq;
+            for (int qq = 0; qq < EPL2; ++qq) moved |= (e[qq] > (qq ? e[qq - 1] : 0.f) ? 1u : 0u) << qq;
+            int lz = moved ? gl * EPL2 + 31 - __clz(moved) : -1;
             lz = group_incl_max<LPT>(lz);
             if (short_tile) {
                 jsel[gmax] = start + max(lz, 0);

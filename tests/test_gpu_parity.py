@@ -212,6 +212,54 @@ def test_prop_budgets(gpu, S):
     _say("S", S, rep)
 
 
+def _offsets_below_tile_edges(dev, S):
+    """Per head, the largest fp32 offset U that puts a systematic threshold
+    U + m/S just below the oracle's CDF at the end of one tile (a different
+    tile per head): the threshold then sits within ~1e-9 of the tile edge,
+    where the fp32 count at the tile's last token can fall one short of
+    the tile's budget."""
+    import oracle as O
+    import parity
+    inp = dev.inp
+    c = inp.cfg
+    prob = parity.oracle_problem(dev)
+    T = dev.problem.s.tile_len
+    u = inp.u(S).astype(np.float32).copy()
+    for bh in range(c.batch * c.num_q_heads):
+        b, h = divmod(bh, c.num_q_heads)
+        e, z, _ = O.softmax_weights(O.logits(prob, inp.q, inp.k, b, h))
+        n = e.size
+        nt = (n + T - 1) // T
+        if nt < 2:
+            continue
+        t = bh % (nt - 1)                        # not the last tile (its C is 1)
+        Ct = float(np.sum(e[: (t + 1) * T], dtype=np.float64) / z)
+        m = int(np.floor(Ct * S))
+        ustar = Ct - m / S                       # U + m/S = C_t exactly
+        uf = np.float32(ustar)
+        if float(uf) >= ustar:
+            uf = np.nextafter(uf, np.float32(0))
+        if float(uf) < 0 or not np.isfinite(uf):
+            continue
+        u[bh] = uf
+    return u
+
+
+@pytest.mark.parametrize("T", [64, 256, 1024])
+def test_prop_thresholds_just_below_tile_edges(gpu, T):
+    """Every head has a threshold within ~1e-9 below a tile's upper CDF edge
+    (its offset U set from the oracle's CDF), so that the fp32 count at the
+    tile's last token lands on either side of the budget: the indices still
+    meet the bar (the tile's last token of nonzero weight, or a neighbour
+    across the edge within 1e-6)."""
+    import parity
+    cfg = synth.small_config(2, batch=2, seq_len=3 * T * 4 + 17)
+    dev = _dev(cfg, 21, gpu, tile_len=T)
+    u = _offsets_below_tile_edges(dev, 128)
+    rep = parity.check_prop(dev, 128, uniforms=u)
+    _say("T", T, rep)
+
+
 def test_prop_tiny_sequences(gpu):
     """n_k = 1 and n_k shorter than one tile."""
     import parity
