@@ -416,7 +416,7 @@ __device__ __forceinline__ void reduce_head(const float2 *__restrict__ stp, cons
         reduce_in_registers<1>(st, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out);
     else if (nt <= 128)
         reduce_in_registers<2>(st, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out);
-    else if (nt <= kRegisterTiles)
+    else if (__builtin_expect(nt <= kRegisterTiles, 1))
         reduce_in_registers<4>(st, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out);
     else
         reduce_with_lds(stp, nt, lane, count, scale, kcap, vis, budget, max_nt, nvis_out, R);
@@ -498,7 +498,9 @@ __device__ __forceinline__ void sample_head(
     const int n = seq_len_of(seq_lens, L.max_seq_len, b);
     const int nt = (n + T - 1) / T;
 
-    if (nt == 0) {                                  // empty request
+    // rare branches are marked unlikely: the compiler then places their
+    // code after the hot path, which spans fewer instruction-cache lines
+    if (__builtin_expect(nt == 0, 0)) {             // empty request
         if (tile_budget)
             for (int t = tid; t < max_nt; t += SB) tile_budget[(size_t)bh * max_nt + t] = 0;
         if (sample_idx)
@@ -775,7 +777,7 @@ __device__ __forceinline__ void sample_head(
         // (the count at the group's last lane, gmax there, is below hi);
         // thresholds gmax .. hi-1 go to the last token whose weight moved P
         const bool short_tile = active && gl == LPT - 1 && gmax < hi;
-        if (__ballot(short_tile)) {
+        if (__builtin_expect(__ballot(short_tile) != 0, 0)) {
             // the lane's tokens that moved P, as bits: one
             // register, where per-token candidate indices were hoisted out
             // of the tile loop by the compiler and spilled
