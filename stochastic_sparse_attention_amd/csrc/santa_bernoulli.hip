@@ -62,6 +62,22 @@ __global__ __launch_bounds__(kBlock) void bernoulli_pass1_kernel(
     if (t0 >= n && tile != 0) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
+    // thread (slot fs, chunk): 4 consecutive keys of the features the slot
+    // streams.  Per head, the group's queries keep nearly every feature
+    // between them, so each slot's first U features in natural order
+    // (fs, fs + FP, ..., all below U * FP <= d) are requested before the
+    // queries are known; a feature that no query keeps then has coefficient
+    // 0.  With the mean query a third of the features are dropped, and none
+    // is read before the list is known.
+    constexpr int U = 8;                         // features in flight per thread
+    constexpr bool SPEC = !MEAN;
+    static_assert(U * FP <= kHeadDim, "speculative features");
+    const int chunk = tid % CH, fs = tid / CH;
+    const int j = t0 + 4 * chunk;
+    const bool jin = j < max_seq_len;            // whole chunk in the row (max_seq_len % 4 == 0)
+    const KV *kbase = kf + ((size_t)b * num_kv_heads + g) * kHeadDim * (size_t)max_seq_len + (jin ? j : 0);
+    typedef typename Chunk4<KV>::type chunk_t;
+
     __shared__ float cq[kHeadDim][NQ];           // c_i of each query, feature-major
     __shared__ float amax[NQ][2];                // max |q_i| over each half of d
     __shared__ float red_m[NQ], red_z[NQ];
@@ -92,6 +108,15 @@ __global__ __launch_bounds__(kBlock) void bernoulli_pass1_kernel(
 #pragma unroll
         for (int hh = 0; hh < QL; ++hh) qraw[k][hh] = qrow[(size_t)(MEAN ? hh : qh) * kHeadDim];
     }
+    // the speculative K loads go behind the query and uniforms, which the
+    // prologue waits for first
+    chunk_t spec[SPEC ? U : 1];
+    if constexpr (SPEC) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            spec[u] = __builtin_nontemporal_load(
+                reinterpret_cast<const chunk_t *>(kbase + (size_t)(fs + u * FP) * max_seq_len));
+    }
 #pragma unroll
     for (int k = 0; k < NE; ++k) {
         const int e = tid + k * kBlock;
@@ -107,7 +132,10 @@ __global__ __launch_bounds__(kBlock) void bernoulli_pass1_kernel(
         }
         qv[k] = ok ? qf : 0.f;
 #pragma unroll
-        for (int r = 0; r < RP; ++r) upre[k][r] = (ok && r < draws) ? upre[k][r] : 0.f;
+        // masked with bits, not a select: a select let the compiler sink a
+        // load into a branch behind the K loads, whose wait then drained them
+        for (int r = 0; r < RP; ++r)
+            upre[k][r] = __int_as_float(__float_as_int(upre[k][r]) & -(int)(ok && r < draws));
         // 64 consecutive entries lie in one half of one query
         const float m = wave_max(fabsf(qv[k]));
         if (lane == 0 && ok) amax[e / kHeadDim][(e % kHeadDim) / 64] = m;
@@ -157,18 +185,33 @@ __global__ __launch_bounds__(kBlock) void bernoulli_pass1_kernel(
     if (t0 >= n) return;   // empty request: only its read count is written
 
     // ---- stream the kept features: slot fs takes list entries fs, fs+FP, ...
-    const int chunk = tid % CH, fs = tid / CH;
-    const int j = t0 + 4 * chunk;
-    const bool jin = j < max_seq_len;            // whole chunk in the row (max_seq_len % 4 == 0)
-    const KV *kbase = kf + ((size_t)b * num_kv_heads + g) * kHeadDim * (size_t)max_seq_len + j;
-    typedef typename Chunk4<KV>::type chunk_t;
     float acc[NQ][4];
 #pragma unroll
     for (int qh = 0; qh < NQ; ++qh)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[qh][e] = 0.f;
-    constexpr int U = 8;                         // features in flight per thread
-    for (int kk = fs; kk < m; kk += U * FP) {
+    int kstart = 0;                              // list entries already added
+    if constexpr (SPEC) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int f = fs + u * FP;
+            float kv[4];
+            widen4(jin ? spec[u] : chunk_t{}, kv);
+#pragma unroll
+            for (int qh = 0; qh < NQ; ++qh) {
+                const float c = cq[f][qh];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[qh][e] = fmaf(c, kv[e], acc[qh][e]);
+            }
+        }
+        // the list then continues with the kept features from U * FP on
+        constexpr int NF = U * FP;
+        if constexpr (NF >= 128) kstart = m;
+        else if constexpr (NF > 64) kstart = __popcll(k0) + __popcll(k1 & ((1ull << (NF - 64)) - 1ull));
+        else if constexpr (NF == 64) kstart = __popcll(k0);
+        else kstart = __popcll(k0 & ((1ull << NF) - 1ull));
+    }
+    for (int kk = kstart + fs; kk < m; kk += U * FP) {
         chunk_t raw[U];
         int fi[U];
 #pragma unroll
