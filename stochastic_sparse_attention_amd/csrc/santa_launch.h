@@ -64,6 +64,8 @@ struct LaunchArgs {
     const float *u_bern;  // [B*Hq or B*Hkv, draws, d] uniforms
     int *features_read;   // [B*Hkv] or null
     int stash_shift;      // prop: 1 << stash_shift consecutive heads share one stash row
+    int sample_parts;     // prop: workgroups per head in the sampling kernel (0 or 1: one;
+                          // 2: two, and pass 1 zeroes out, which both add into)
     Workspace ws;
     void *stream;
 };
@@ -72,6 +74,13 @@ struct TimingHook {
     void *begin;
     void *end;
 };
+
+// Up to this many q heads per call, prop's sampling kernel (systematic
+// thresholds) gives each head two workgroups: at most two 16-wave
+// workgroups per compute unit, which fit together.  The output of a head
+// can differ in its last bits between calls above and below this count
+// (the two halves are added in another order).
+constexpr int kSampleSplitHeads = 256;
 
 // One decode call: the launches for a.kv_dtype (santa_dispatch.cpp).
 hipError_t launch_prop(const LaunchArgs &a, const TimingHook &hook);

@@ -23,19 +23,21 @@
 
 namespace santa {
 
-// One workgroup per (request, q head): block bg + i * B*Hkv takes head i of
-// the group of (request, KV head) bg.
+// One workgroup per (request, q head), or two (nparts = 2): block
+// part * B*Hq + bg + i * B*Hkv takes head i of the group of (request, KV
+// head) bg.
 template <typename KV, int T, bool PAGED, bool LIST, int NW>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(LIST ? 4 : 8))) void prop_sample_kernel(
     const KV *__restrict__ v, KVLayout L, const int *__restrict__ seq_lens, int batch, int num_q_heads,
     int G, int S, int max_nt, int kcap, int sampler, const float *__restrict__ u, float scale,
     const float *__restrict__ stash, const float2 *__restrict__ stats, float *__restrict__ out,
-    int *__restrict__ sample_idx, int *__restrict__ tile_budget, int stash_shift) {
-    const int BG = batch * L.num_kv_heads;
-    const int bg = blockIdx.x % BG, hl = blockIdx.x / BG;
+    int *__restrict__ sample_idx, int *__restrict__ tile_budget, int stash_shift, int nparts) {
+    const int BG = batch * L.num_kv_heads, BH = batch * num_q_heads;
+    const int part = blockIdx.x / BH, hb = blockIdx.x - part * BH;
+    const int bg = hb % BG, hl = hb / BG;
     const int b = bg / L.num_kv_heads, g = bg - b * L.num_kv_heads;
     sample_head<KV, T, PAGED, LIST, NW>(v, L, seq_lens, num_q_heads, G, S, max_nt, kcap, sampler, u, scale, stash,
-                                        stats, out, sample_idx, tile_budget, stash_shift, b, g, hl);
+                                        stats, out, sample_idx, tile_budget, stash_shift, b, g, hl, part, nparts);
 }
 
 // ===================================================================
@@ -50,6 +52,7 @@ static hipError_t launch_sample_t(const LaunchArgs &a, const TimingHook &) {
     float2 *stats = (float2 *)a.ws.stats;
     const KVLayout L = layout_of(a);
     const int BH = a.batch * a.num_q_heads;
+    const int nparts = a.sample_parts > 1 ? 2 : 1;
     const size_t lds = prop_sample_lds_bytes(a.kmax, a.S, a.sampler, max_nt);
     // few heads: 16 waves per head; many heads: 8, so that more heads (and
     // their dependent memory round trips) share each compute unit
@@ -60,10 +63,10 @@ static hipError_t launch_sample_t(const LaunchArgs &a, const TimingHook &) {
                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (ea != hipSuccess) return ea;
         }
-        hipLaunchKernelGGL(kernel, dim3((unsigned)BH), dim3(nw * kWave), lds, st, (const KV *)a.v, L, a.seq_lens,
-                           a.batch, a.num_q_heads, G, a.S, max_nt, a.kmax, a.sampler, a.u, a.scale,
+        hipLaunchKernelGGL(kernel, dim3((unsigned)(BH * nparts)), dim3(nw * kWave), lds, st, (const KV *)a.v, L,
+                           a.seq_lens, a.batch, a.num_q_heads, G, a.S, max_nt, a.kmax, a.sampler, a.u, a.scale,
                            (const float *)stash, (const float2 *)stats, a.out, a.sample_idx, a.tile_budget,
-                           a.stash_shift);
+                           a.stash_shift, nparts);
         return hipGetLastError();
     };
     if (a.sampler != kSamplerSys)

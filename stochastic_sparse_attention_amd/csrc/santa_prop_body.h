@@ -463,7 +463,8 @@ __device__ __forceinline__ void sample_head(
     const KV *__restrict__ v, KVLayout L, const int *__restrict__ seq_lens, int num_q_heads,
     int G, int S, int max_nt, int kcap, int sampler, const float *__restrict__ u, float scale,
     const float *__restrict__ stash, const float2 *__restrict__ stats, float *__restrict__ out,
-    int *__restrict__ sample_idx, int *__restrict__ tile_budget, int stash_shift, int b, int g, int hl) {
+    int *__restrict__ sample_idx, int *__restrict__ tile_budget, int stash_shift, int b, int g, int hl,
+    int part, int nparts) {
     constexpr int SB = NW * kWave;                  // threads per workgroup
     extern __shared__ __align__(16) unsigned char smem[];
     // stratified / i.i.d.: the sorted thresholds first (padded to a power of
@@ -606,7 +607,7 @@ __device__ __forceinline__ void sample_head(
     if (w != 0) {
         for (int m = tid - kWave; m < S; m += SB - kWave) jsel[m] = -1;
     } else {
-        int *budget = tile_budget ? tile_budget + (size_t)bh * max_nt : nullptr;
+        int *budget = tile_budget && part == 0 ? tile_budget + (size_t)bh * max_nt : nullptr;
         const ReducerLds R{tstat, tf, tC, tcn};
         if constexpr (!LIST)
             reduce_head(stp, st, nt, lane, SysCount{clamp_offset(u_sys, S), S}, scale, kcap, vis, budget, max_nt, nvis_sh, R);
@@ -670,8 +671,10 @@ __device__ __forceinline__ void sample_head(
             wave_sync_lds();
         }
     };
-    const bool multi = nvis > TPW * NW;        // some wave takes more than one round of tiles
-    for (int k0 = w * TPW; k0 < nvis; k0 += TPW * NW) {
+    // with two workgroups per head (nparts = 2, part 0 or 1), workgroup p
+    // takes rounds p, p + 2, ... of TPW * NW visited tiles
+    const bool multi = nvis > TPW * NW * nparts;   // some wave takes more than one round of tiles
+    for (int k0 = (part * NW + w) * TPW; k0 < nvis; k0 += TPW * NW * nparts) {
         const int kv = k0 + sub;
         const bool active = kv < nvis;
         const VisitRec rec = vis[active ? kv : k0];
@@ -817,23 +820,32 @@ __device__ __forceinline__ void sample_head(
         __syncthreads();
         for (int c = w * kWave; c < S; c += NW * kWave) gather_range(c, min(c + kWave, S));
     }
+    // One workgroup per head, or one round of the first covering every
+    // visited tile: the first stores the head's output.  Otherwise both add
+    // their halves into the output row that pass 1 zeroed: two addends onto
+    // zero give the same sum in either order.
+    const bool alone = nparts == 1 || nvis <= TPW * NW;
+    if (!alone || part == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        acc[e] += __shfl_xor(acc[e], 16);
-        acc[e] += __shfl_xor(acc[e], 32);
-    }
-    if (lane < 16) {
+        for (int e = 0; e < 8; ++e) {
+            acc[e] += __shfl_xor(acc[e], 16);
+            acc[e] += __shfl_xor(acc[e], 32);
+        }
+        if (lane < 16) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) red[w][8 * chunk + e] = acc[e];
-    }
-    __syncthreads();
-    if (tid < kHeadDim) {
-        float sum = 0.f;
+            for (int e = 0; e < 8; ++e) red[w][8 * chunk + e] = acc[e];
+        }
+        __syncthreads();
+        if (tid < kHeadDim) {
+            float sum = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) sum += red[ww][tid];
-        // divide by S: for a power of two this is an exact exponent shift
-        const bool pow2 = (S & (S - 1)) == 0;
-        out[(size_t)bh * kHeadDim + tid] = pow2 ? sum * (1.0f / (float)S) : sum / (float)S;
+            for (int ww = 0; ww < NW; ++ww) sum += red[ww][tid];
+            // divide by S: for a power of two this is an exact exponent shift
+            const bool pow2 = (S & (S - 1)) == 0;
+            const float r = pow2 ? sum * (1.0f / (float)S) : sum / (float)S;
+            if (alone) out[(size_t)bh * kHeadDim + tid] = r;
+            else atomicAdd(out + (size_t)bh * kHeadDim + tid, r);
+        }
     }
 }
 

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kBlock) void prop_fused_kernel(
             for (int hl = 0; hl < G; ++hl)
                 sample_head<KV, T, PAGED, false, kWavesPerBlock>(v, L, seq_lens, num_q_heads, G, S, max_nt, kcap,
                                                                  kSamplerSys, u, scale, stash, stats, out,
-                                                                 sample_idx, tile_budget, 0, b, g, hl);
+                                                                 sample_idx, tile_budget, 0, b, g, hl, 0, 1);
         return;
     }
     if (tile >= nt) return;
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kBlock) void prop_fused_kernel(
         if (hl) __syncthreads();
         sample_head<KV, T, PAGED, false, kWavesPerBlock>(v, L, seq_lens, num_q_heads, G, S, max_nt, kcap,
                                                          kSamplerSys, u, scale, stash, stats, out, sample_idx,
-                                                         tile_budget, 0, b, g, hl);
+                                                         tile_budget, 0, b, g, hl, 0, 1);
     }
 }
 

@@ -14,9 +14,15 @@ namespace santa {
 template <typename KV, int G, int T, bool PAGED>
 __global__ __launch_bounds__(kBlock) void prop_pass1_kernel(
     const typename QOf<KV>::type *__restrict__ q, const KV *__restrict__ k, KVLayout L, const int *__restrict__ seq_lens,
-    int num_q_heads, int max_nt, float scale, float *__restrict__ stash, float2 *__restrict__ stats) {
+    int num_q_heads, int max_nt, float scale, float *__restrict__ stash, float2 *__restrict__ stats,
+    float *__restrict__ zero_out) {
     int tile, b, g;
     tile_of_block<PAGED>(L, max_nt, tile, b, g);
+    // when the sampling kernel adds two workgroups' halves into out, the
+    // group's tile-0 workgroup zeroes the group's output rows first
+    if (zero_out && tile == 0)
+        for (int i = threadIdx.x; i < G * kHeadDim; i += kBlock)
+            zero_out[((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim + i] = 0.f;
     const int n = seq_len_of(seq_lens, L.max_seq_len, b);
     if (tile * T >= n) return;
     pass1_tile<KV, G, T, PAGED>(q, k, L, n, num_q_heads, max_nt, scale, stash, stats, tile, b, g);
@@ -29,16 +35,17 @@ static hipError_t launch_pass1_t(const LaunchArgs &a, const TimingHook &hook) {
     float *stash = (float *)a.ws.stash;
     float2 *stats = (float2 *)a.ws.stats;
     const KVLayout L = layout_of(a);
+    float *zero_out = a.sample_parts > 1 ? a.out : nullptr;
     // with a timing hook the dispatch itself records the two events, so
     // they bracket the kernel's execution and nothing else
     if (hook.begin)
         hipExtLaunchKernelGGL((prop_pass1_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * max_nt)), dim3(kBlock), 0, st, (hipEvent_t)hook.begin, (hipEvent_t)hook.end, 0,
                        (const typename QOf<KV>::type *)a.q, (const KV *)a.k, L, a.seq_lens, a.num_q_heads, max_nt, a.scale,
-                       stash, stats);
+                       stash, stats, zero_out);
     else
         hipLaunchKernelGGL((prop_pass1_kernel<KV, G, T, PAGED>), dim3((unsigned)(a.batch * a.num_kv_heads * max_nt)), dim3(kBlock), 0, st,
                        (const typename QOf<KV>::type *)a.q, (const KV *)a.k, L, a.seq_lens, a.num_q_heads, max_nt, a.scale,
-                       stash, stats);
+                       stash, stats, zero_out);
     return hipGetLastError();
 }
 
