@@ -75,12 +75,14 @@ struct TimingHook {
     void *end;
 };
 
-// Up to this many q heads per call, prop's sampling kernel (systematic
-// thresholds) gives each head two workgroups: at most two 16-wave
-// workgroups per compute unit, which fit together.  The output of a head
+// Up to this many q heads per call, prop's sampling kernel gives each head
+// two workgroups: systematic thresholds, at most two 16-wave workgroups per
+// compute unit (they fit together); stratified and i.i.d. thresholds, whose
+// workgroups take a whole compute unit, at most one.  The output of a head
 // can differ in its last bits between calls above and below this count
 // (the two halves are added in another order).
 constexpr int kSampleSplitHeads = 256;
+constexpr int kSampleListSplitHeads = 128;
 
 // One decode call: the launches for a.kv_dtype (santa_dispatch.cpp).
 hipError_t launch_prop(const LaunchArgs &a, const TimingHook &hook);
