@@ -671,10 +671,12 @@ __device__ __forceinline__ void sample_head(
             wave_sync_lds();
         }
     };
-    // with two workgroups per head (nparts = 2, part 0 or 1), workgroup p
-    // takes rounds p, p + 2, ... of TPW * NW visited tiles
+    // with two workgroups per head (nparts = 2, part 0 or 1), the TPW-tile
+    // groups alternate between them: wave w of workgroup p takes groups
+    // 2 w + p, 2 w + p + 2 NW, ..., so each compute unit serves half of the
+    // head's stash and V loads even when one round would cover every tile
     const bool multi = nvis > TPW * NW * nparts;   // some wave takes more than one round of tiles
-    for (int k0 = (part * NW + w) * TPW; k0 < nvis; k0 += TPW * NW * nparts) {
+    for (int k0 = (w * nparts + part) * TPW; k0 < nvis; k0 += TPW * NW * nparts) {
         const int kv = k0 + sub;
         const bool active = kv < nvis;
         const VisitRec rec = vis[active ? kv : k0];
@@ -820,11 +822,11 @@ __device__ __forceinline__ void sample_head(
         __syncthreads();
         for (int c = w * kWave; c < S; c += NW * kWave) gather_range(c, min(c + kWave, S));
     }
-    // One workgroup per head, or one round of the first covering every
-    // visited tile: the first stores the head's output.  Otherwise both add
-    // their halves into the output row that pass 1 zeroed: two addends onto
-    // zero give the same sum in either order.
-    const bool alone = nparts == 1 || nvis <= TPW * NW;
+    // One workgroup per head, or one tile group in all (the second
+    // workgroup then has none): the first stores the head's output.
+    // Otherwise both add their halves into the output row that pass 1
+    // zeroed: two addends onto zero give the same sum in either order.
+    const bool alone = nparts == 1 || nvis <= TPW;
     if (!alone || part == 0) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
