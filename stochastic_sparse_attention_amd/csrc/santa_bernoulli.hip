@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kBlock) void bernoulli_pass1_kernel(
     const uint16_t *__restrict__ q, const KV *__restrict__ kf, int num_kv_heads, int max_seq_len,
     const int *__restrict__ seq_lens, int num_q_heads, int max_nt, float scale, int draws,
     const float *__restrict__ ub, float *__restrict__ stash, float2 *__restrict__ stats,
-    int *__restrict__ features_read) {
+    int *__restrict__ features_read, float *__restrict__ zero_out) {
     constexpr int NQ = MEAN ? 1 : G;           // ternary queries of the group
     constexpr int CH = T / 4;                  // 4-token chunks in a tile's feature run
     constexpr int FP = kBlock / CH;            // feature slots working side by side
@@ -285,6 +285,12 @@ __global__ __launch_bounds__(kBlock) void bernoulli_pass1_kernel(
         const int qh = MEAN ? 0 : tid;
         stats[((size_t)b * num_q_heads + (size_t)g * G + tid) * max_nt + tile] = make_float2(red_m[qh], red_z[qh]);
     }
+    // when the sampling kernel adds two workgroups' halves into out, the
+    // group's tile-0 workgroup zeroes the group's output rows (last, off the
+    // path of its loads; an empty request's rows are written by the sampler)
+    if (zero_out && tile == 0)
+        for (int i = tid; i < G * kHeadDim; i += kBlock)
+            zero_out[((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim + i] = 0.f;
 }
 
 template <typename KV, int G, int T, bool MEAN>
@@ -296,12 +302,12 @@ static hipError_t launch_bern_t(const LaunchArgs &a, const TimingHook &hook) {
                               (hipEvent_t)hook.begin, (hipEvent_t)hook.end, 0, (const uint16_t *)a.q,
                               (const KV *)a.k, a.num_kv_heads, a.max_seq_len, a.seq_lens, a.num_q_heads,
                               a.max_nt, a.scale, a.draws, a.u_bern, (float *)a.ws.stash, (float2 *)a.ws.stats,
-                              a.features_read);
+                              a.features_read, a.sample_parts > 1 ? a.out : nullptr);
     else
         hipLaunchKernelGGL((bernoulli_pass1_kernel<KV, G, T, MEAN>), grid, dim3(kBlock), 0, st, (const uint16_t *)a.q,
                            (const KV *)a.k, a.num_kv_heads, a.max_seq_len, a.seq_lens, a.num_q_heads,
                            a.max_nt, a.scale, a.draws, a.u_bern, (float *)a.ws.stash, (float2 *)a.ws.stats,
-                           a.features_read);
+                           a.features_read, a.sample_parts > 1 ? a.out : nullptr);
     return hipGetLastError();
 }
 

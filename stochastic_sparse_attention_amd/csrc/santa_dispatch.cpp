@@ -29,7 +29,9 @@ hipError_t launch_prop(const LaunchArgs &a0, const TimingHook &hook) {
     return launch_sample(a, hook);
 }
 
-hipError_t launch_prop_bernoulli(const LaunchArgs &a, const TimingHook &hook) {
+hipError_t launch_prop_bernoulli(const LaunchArgs &a0, const TimingHook &hook) {
+    LaunchArgs a = a0;
+    a.sample_parts = a.batch * a.num_q_heads <= kSampleSplitHeads ? 2 : 1;
     const hipError_t e = launch_bernoulli_pass1(a, hook);
     if (e != hipSuccess) return e;
     return launch_sample(a, hook);

@@ -18,14 +18,15 @@ __global__ __launch_bounds__(kBlock) void prop_pass1_kernel(
     float *__restrict__ zero_out) {
     int tile, b, g;
     tile_of_block<PAGED>(L, max_nt, tile, b, g);
-    // when the sampling kernel adds two workgroups' halves into out, the
-    // group's tile-0 workgroup zeroes the group's output rows first
-    if (zero_out && tile == 0)
-        for (int i = threadIdx.x; i < G * kHeadDim; i += kBlock)
-            zero_out[((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim + i] = 0.f;
     const int n = seq_len_of(seq_lens, L.max_seq_len, b);
     if (tile * T >= n) return;
     pass1_tile<KV, G, T, PAGED>(q, k, L, n, num_q_heads, max_nt, scale, stash, stats, tile, b, g);
+    // when the sampling kernel adds two workgroups' halves into out, the
+    // group's tile-0 workgroup zeroes the group's output rows (last, off the
+    // path of its loads; an empty request's rows are written by the sampler)
+    if (zero_out && tile == 0)
+        for (int i = threadIdx.x; i < G * kHeadDim; i += kBlock)
+            zero_out[((size_t)b * num_q_heads + (size_t)g * G) * kHeadDim + i] = 0.f;
 }
 
 template <typename KV, int G, int T, bool PAGED>
