@@ -25,8 +25,15 @@
  *     null stream).  Results are valid once the stream has synchronised.
  *   - Arguments are validated on the host before anything is launched.  On
  *     any error nothing is launched and no output is written.
- *   - For identical inputs results are bitwise identical from run to run (no
- *     floating-point atomics; every reduction has a fixed order).
+ *   - For identical inputs results are bitwise identical from run to run:
+ *     every reduction has a fixed order, and the only floating-point atomics
+ *     (prop with at most 256 heads in the batch, 128 with the list
+ *     generators) add a head's two partial outputs onto its zeroed row,
+ *     a sum that does not depend on which arrives first.
+ *   - No output may share memory with an input or with another output.  The
+ *     host rejects an `out` that overlaps `q` or the first B*Hq floats of `u`
+ *     with SANTA_ERR_INVALID (prop clears output rows while other
+ *     workgroups of the same call still read the query).
  *   - No C++ exception crosses this boundary.
  *
  * Layouts (row-major, last index fastest)

@@ -21,6 +21,21 @@ thread_local void *g_ev_end = nullptr;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// whether the byte ranges [a, a + na) and [b, b + nb) share a byte
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// `out` must not overlap the query or the per-head offsets: prop's pass 1
+// clears output rows while other workgroups of the call still read q
+bool out_aliases_inputs(const santa_problem *p, const void *q, const float *u, const float *out) {
+    const size_t rows = (size_t)p->batch * p->num_q_heads;
+    const size_t out_bytes = rows * p->head_dim * sizeof(float);
+    const size_t q_bytes = rows * p->head_dim * (p->q_dtype == SANTA_F32 ? 4 : 2);
+    return overlaps(out, out_bytes, q, q_bytes) || (u && overlaps(out, out_bytes, u, rows * sizeof(float)));
+}
+
 struct Derived {
     int group = 0;
     int max_nt = 0;
@@ -154,6 +169,7 @@ int run_sampled(int variant, const santa_problem *p, const void *q, const void *
         return SANTA_ERR_INVALID;
     if (p->batch == 0) return SANTA_OK;
     if (!q || !k || !v || !u || !out) return SANTA_ERR_INVALID;
+    if (out_aliases_inputs(p, q, u, out)) return SANTA_ERR_INVALID;
     santa::Workspace ws;
     st = check_workspace(p, variant, d, workspace, workspace_bytes, &ws);
     if (st != SANTA_OK) return st;
@@ -196,6 +212,7 @@ int santa_decode_prop_fused(const santa_problem *p, const void *q, const void *k
     if ((long)p->batch * p->num_kv_heads > santa::kMaxSyncGroups) return SANTA_ERR_UNSUPPORTED;
     if (p->batch == 0) return SANTA_OK;
     if (!q || !k || !v || !u || !out) return SANTA_ERR_INVALID;
+    if (out_aliases_inputs(p, q, u, out)) return SANTA_ERR_INVALID;
     santa::Workspace ws;
     st = check_workspace(p, SANTA_VARIANT_PROP, d, workspace, workspace_bytes, &ws);
     if (st != SANTA_OK) return st;
@@ -235,6 +252,7 @@ int exact_decode_ref(const santa_problem *p, const void *q, const void *k, const
     if (st != SANTA_OK) return st;
     if (p->batch == 0) return SANTA_OK;
     if (!q || !k || !v || !out) return SANTA_ERR_INVALID;
+    if (out_aliases_inputs(p, q, nullptr, out)) return SANTA_ERR_INVALID;
     santa::Workspace ws;
     st = check_workspace(p, SANTA_VARIANT_EXACT, d, workspace, workspace_bytes, &ws);
     if (st != SANTA_OK) return st;
@@ -259,6 +277,7 @@ int santa_decode_prop_bernoulli(const santa_problem *p, const void *q, const voi
     if (!q || !k_features || !v || !u || !u_bern || !out) return SANTA_ERR_INVALID;
     // 4 keys of a feature per lane load: 8 bytes of bf16, 4 of e4m3
     if (((uintptr_t)k_features) % (p->kv_dtype == SANTA_BF16 ? 8 : 4)) return SANTA_ERR_INVALID;
+    if (out_aliases_inputs(p, q, u, out)) return SANTA_ERR_INVALID;
     santa::Workspace ws;
     st = check_workspace(p, SANTA_VARIANT_PROP, d, workspace, workspace_bytes, &ws);
     if (st != SANTA_OK) return st;

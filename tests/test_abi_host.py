@@ -15,6 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
 PROP, FLASH, EXACT = 0, 1, 2
 DUMMY = C.c_void_p(0x100000)          # never dereferenced: validation fails first
+OUT = C.c_void_p(0x300000000)         # an output apart from every input
 
 
 def _header_functions():
@@ -49,16 +50,16 @@ def _wsize(lib, p, variant, S):
     return st, n.value
 
 
-def _prop(lib, p, S=128, ws_bytes=1 << 30, ws=DUMMY, out=DUMMY, u=DUMMY, q=DUMMY):
+def _prop(lib, p, S=128, ws_bytes=1 << 30, ws=DUMMY, out=OUT, u=DUMMY, q=DUMMY):
     return lib.santa_decode_prop(C.byref(p), q, DUMMY, DUMMY, S, u, out, None, None, ws, ws_bytes, None)
 
 
 def _flash(lib, p, S=2048, ws_bytes=1 << 30):
-    return lib.santa_decode_flash(C.byref(p), DUMMY, DUMMY, DUMMY, S, DUMMY, DUMMY, None, None, DUMMY,
+    return lib.santa_decode_flash(C.byref(p), DUMMY, DUMMY, DUMMY, S, DUMMY, OUT, None, None, DUMMY,
                                   ws_bytes, None)
 
 
-def _exact(lib, p, ws_bytes=1 << 30, out=DUMMY):
+def _exact(lib, p, ws_bytes=1 << 30, out=OUT):
     return lib.exact_decode_ref(C.byref(p), DUMMY, DUMMY, DUMMY, out, DUMMY, ws_bytes, None)
 
 
@@ -126,15 +127,15 @@ def test_fp8_kv_accepted(lib):
 def test_sampler_validation(lib):
     p = _problem()
     for bad in (-1, 3, 99):
-        assert lib.santa_decode_prop_sampler(C.byref(p), DUMMY, DUMMY, DUMMY, 128, bad, DUMMY, DUMMY, None,
+        assert lib.santa_decode_prop_sampler(C.byref(p), DUMMY, DUMMY, DUMMY, 128, bad, DUMMY, OUT, None,
                                              None, DUMMY, 1 << 30, None) == INVALID
     # the sampler call shares the problem and workspace checks of prop
     assert lib.santa_decode_prop_sampler(C.byref(_problem(tile_len=100)), DUMMY, DUMMY, DUMMY, 128, 1, DUMMY,
-                                         DUMMY, None, None, DUMMY, 1 << 30, None) == INVALID
-    assert lib.santa_decode_prop_sampler(C.byref(p), DUMMY, DUMMY, DUMMY, 128, 2, DUMMY, DUMMY, None, None,
+                                         OUT, None, None, DUMMY, 1 << 30, None) == INVALID
+    assert lib.santa_decode_prop_sampler(C.byref(p), DUMMY, DUMMY, DUMMY, 128, 2, DUMMY, OUT, None, None,
                                          DUMMY, 10, None) == WORKSPACE
     assert lib.santa_decode_prop_sampler(C.byref(_problem(batch=0)), DUMMY, DUMMY, DUMMY, 128, 1, DUMMY,
-                                         DUMMY, None, None, DUMMY, 1 << 30, None) == OK
+                                         OUT, None, None, DUMMY, 1 << 30, None) == OK
 
 
 def test_pointer_and_workspace_validation(lib):
@@ -153,6 +154,30 @@ def test_pointer_and_workspace_validation(lib):
     n = C.c_size_t(0)
     assert lib.santa_workspace_size(C.byref(p), 9, 128, C.byref(n)) == INVALID
     assert lib.santa_workspace_size(C.byref(p), PROP, 128, None) == INVALID
+
+
+def test_output_overlapping_an_input_is_rejected(lib):
+    """`out` may not share a byte with q or with the B*Hq offsets of u (prop
+    clears output rows while other workgroups still read the query).  The
+    workspace is too small throughout, so a call that passed the overlap
+    check would stop at WORKSPACE before any launch."""
+    p = _problem()                                   # q: 32*128 bf16 = 8 KiB; out: 16 KiB; u: 128 B
+    q0 = 0x200000000
+    for out in (q0, q0 + 8191, q0 - 16383):          # first byte, last byte, overlap from below
+        assert _prop(lib, p, ws_bytes=10, q=C.c_void_p(q0), out=C.c_void_p(out)) == INVALID
+        assert _exact(lib, p, ws_bytes=10, out=C.c_void_p(out)) == WORKSPACE   # q is DUMMY there
+    for out in (q0 + 8192, q0 - 16384):              # adjacent on either side: allowed
+        assert _prop(lib, p, ws_bytes=10, q=C.c_void_p(q0), out=C.c_void_p(out)) == WORKSPACE
+    assert _prop(lib, p, ws_bytes=10, u=C.c_void_p(0x400000040), out=C.c_void_p(0x400000000)) == INVALID
+    assert _prop(lib, p, ws_bytes=10, u=C.c_void_p(0x400004000), out=C.c_void_p(0x400000000)) == WORKSPACE
+    assert lib.exact_decode_ref(C.byref(p), DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 10, None) == INVALID
+    assert lib.santa_decode_flash(C.byref(p), DUMMY, DUMMY, DUMMY, 2048, OUT, DUMMY, None, None, DUMMY, 10,
+                                  None) == INVALID                    # out == q
+    assert lib.santa_decode_prop_fused(C.byref(p), DUMMY, DUMMY, DUMMY, 128, DUMMY, DUMMY, None, None, DUMMY,
+                                       10, None) == INVALID
+    assert _bern(lib, p, ws_bytes=10) == WORKSPACE
+    assert lib.santa_decode_prop_bernoulli(C.byref(p), DUMMY, DUMMY, DUMMY, 128, DUMMY, 4, 0, DUMMY, DUMMY,
+                                           None, None, None, DUMMY, 10, None) == INVALID
 
 
 def test_empty_batch_is_a_noop(lib):
@@ -179,7 +204,7 @@ def test_binding_raises_on_error(lib):
 
 
 def _bern(lib, p, S=128, draws=4, gm=0, kf=DUMMY, ub=DUMMY, ws_bytes=1 << 30):
-    return lib.santa_decode_prop_bernoulli(C.byref(p), DUMMY, kf, DUMMY, S, DUMMY, draws, gm, ub, DUMMY,
+    return lib.santa_decode_prop_bernoulli(C.byref(p), DUMMY, kf, DUMMY, S, DUMMY, draws, gm, ub, OUT,
                                            None, None, None, DUMMY, ws_bytes, None)
 
 
@@ -204,7 +229,7 @@ def test_bernoulli_entry_validates_before_launch(lib):
 
 
 def _prop_fused(lib, p, S=128, ws_bytes=1 << 30):
-    return lib.santa_decode_prop_fused(C.byref(p), DUMMY, DUMMY, DUMMY, S, DUMMY, DUMMY, None, None, DUMMY,
+    return lib.santa_decode_prop_fused(C.byref(p), DUMMY, DUMMY, DUMMY, S, DUMMY, OUT, None, None, DUMMY,
                                        ws_bytes, None)
 
 
