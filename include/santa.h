@@ -20,7 +20,8 @@
  * Conventions shared by every entry point
  *   - Every pointer argument is a DEVICE pointer unless its comment says host.
  *   - The caller owns all memory.  The library allocates nothing, keeps no
- *     global state except the optional timing hook below, and is reentrant.
+ *     global state except the optional timing hook and the static scratch
+ *     of santa_decode_prop_static (both below), and is reentrant.
  *   - Work is launched asynchronously on `stream` (a hipStream_t; NULL is the
  *     null stream).  Results are valid once the stream has synchronised.
  *   - Arguments are validated on the host before anything is launched.  On
@@ -29,7 +30,10 @@
  *     every reduction has a fixed order, and the only floating-point atomics
  *     (prop with at most 256 heads in the batch, 128 with the list
  *     generators) add a head's two partial outputs onto its zeroed row,
- *     a sum that does not depend on which arrives first.
+ *     a sum that does not depend on which arrives first.  A head's output
+ *     can differ in its last bits between calls on either side of those
+ *     head counts (its partial sums are grouped differently); its indices
+ *     and budgets do not.
  *   - No output may share memory with an input or with another output.  The
  *     host rejects an `out` that overlaps `q` or the first B*Hq floats of `u`
  *     with SANTA_ERR_INVALID (prop clears output rows while other
