@@ -524,6 +524,50 @@ def test_kv_cache_past_2_pow_31_elements(gpu):
     _say("offsets past 2^31 elements: last request bitwise equal (prop, flash, exact)")
 
 
+@pytest.mark.parametrize("sampler,B", [("sys", 9), ("strat", 5)])
+def test_prop_split_heads_match_one_workgroup_per_head(gpu, sampler, B):
+    """Up to 256 heads per call (128 with the list generators) each head's
+    pass 2 runs on two workgroups whose halves are added onto the output row
+    that pass 1 zeroed; above that one workgroup takes the head.  One request
+    of flat attention (nearly every tile visited, so both halves add) is run
+    alone (split, held to the oracle bar) and repeated B times (more heads
+    than the limit): every copy must give the same indices and budgets
+    bitwise, and the same output up to its last bits."""
+    import torch
+    import parity
+    import stochastic_sparse_attention_amd as sa
+    cfg = synth.small_config(8, seq_len=8192)
+    dev = _dev(cfg, 43, gpu)
+    S, H, Hkv, n, d = cfg.S, cfg.num_q_heads, cfg.num_kv_heads, cfg.seq_len, cfg.head_dim
+    T = dev.problem.s.tile_len
+    nt = n // T
+    assert H <= 128 < B * H and (sampler != "sys" or B * H > 256)
+    _say("split heads, alone vs oracle", sampler, parity.check_prop(dev, S, repeat=False, sampler=sampler))
+    out_s, idx_s, tb_s = parity.run_prop(dev, S, sampler=sampler)
+    assert (tb_s > 0).sum(axis=1).min() > 4          # more tile groups than one, so both halves add
+    q = dev.q.view(1, H, d).repeat(B, 1, 1).contiguous()
+    k = dev.k.view(1, Hkv, n, d).repeat(B, 1, 1, 1).contiguous()
+    v = dev.v.view(1, Hkv, n, d).repeat(B, 1, 1, 1).contiguous()
+    prob = sa.Problem(B, H, Hkv, d, n, dtype="bf16", scale=dev.inp.scale, tile_len=T)
+    out = torch.full((B * H, d), float("nan"), dtype=torch.float32, device=gpu)
+    idx = torch.full((B * H, S), -7, dtype=torch.int32, device=gpu)
+    tb = torch.full((B * H, nt), -7, dtype=torch.int32, device=gpu)
+    if sampler == "sys":
+        sa.santa_decode_prop(prob, q, k, v, S, dev.u(S).repeat(B), out, idx, tb)
+    else:
+        sa.santa_decode_prop_sampler(prob, q, k, v, S, sampler, dev.uniforms(S).repeat(B, 1), out, idx, tb)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().reshape(B, H, d)
+    ii = idx.cpu().numpy().reshape(B, H, S)
+    bb = tb.cpu().numpy().reshape(B, H, nt)
+    for r in range(B):
+        assert np.array_equal(ii[r], idx_s) and np.array_equal(bb[r], tb_s), r
+        assert np.array_equal(o[r].view(np.uint32), o[0].view(np.uint32)), r
+    err = float(np.abs(o[0] - out_s).max())
+    assert err <= 1e-6 * float(np.abs(out_s).max()) + 1e-7, err
+    _say(f"split heads ({sampler}, {B} copies): indices and budgets equal, output max diff {err:.3g}")
+
+
 # ------------------------------------------------- Bernoulli qK^T + prop
 @pytest.mark.parametrize("T", [64, 256, 1024])
 @pytest.mark.parametrize("draws,group_mean", [(1, 0), (4, 0), (4, 1), (16, 1)])
