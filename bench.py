@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -39,10 +40,16 @@ KERNEL_SOURCES = ["santa_prop_pass1.hip", "santa_prop_body.h", "santa_kernels.h"
 
 
 def kernel_source_hash():
+    """Hash of the code (comments and blank lines removed) of the sources
+    that pass 1 is built from, so that a comment edit keeps the counters."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "stochastic_sparse_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "stochastic_sparse_attention_amd", "csrc", f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        code = "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 

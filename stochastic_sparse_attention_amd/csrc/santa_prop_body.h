@@ -98,7 +98,11 @@ __device__ __forceinline__ void pass1_tile(
 
 // ===================================================================
 // S2ANTA-prop, reducer + pass 2: one workgroup per (request, q head), of
-// 16 waves (8 with many heads).  No cross-workgroup communication.
+// 16 waves (8 or 4 with many heads), or two (part 0 and 1 of nparts = 2)
+// when heads are few.  Both parts run the reducer; their waves take
+// alternate groups of visited tiles, and each adds its share of the output
+// onto the row that pass 1 zeroed (two addends onto zero: the same sum in
+// either order).  Nothing else passes between workgroups.
 // ===================================================================
 // Reducer (wave 0; lane l owns tiles [l CH, l CH + CH), CH = ceil(n_t/64),
 // n_t <= 1024): global max M of the tile maxima, tile masses
