@@ -39,7 +39,9 @@ import time
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB names another build of the same source (the planted-mistake
+# test loads altered copies that way); by default the one built here
+LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 
 # storage formats of the oracle's problem struct
@@ -64,6 +66,8 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
+            if os.environ.get("ORACLE_LIB"):
+                raise FileNotFoundError(LIB_PATH)
             from . import build as _b
             _b.build()
         L = C.CDLL(LIB_PATH)

@@ -847,6 +847,29 @@ def test_bernoulli_group_union_and_mean_query():
     assert x0.tolist() == x1.tolist() == [1.0 - 2.0 + 8.0, 0.5 + 1.0 - 2.0]
 
 
+def test_bernoulli_mean_query_uses_its_groups_uniforms():
+    """Two KV groups of two heads (uniforms [B*Hkv, draws, d]).  Group 1's
+    mean query is [0.5, 0.5, -1, 0.25] (a = 1); its own uniforms [0.25, 0.75,
+    0.9, 0.1] keep features 0, 2 and 3, c = [1, 0, -1, 1], so both of its
+    heads score its keys [1, 2, 4, 8] and [0.5, -1, 3, -2] as 1 - 4 + 8 = 5
+    and 0.5 - 3 - 2 = -4.5.  Group 0's uniforms [0.75, 0.25, 0.9, 0.5] would
+    give c = [0, 1, -1, 0] instead.  Group 0's mean query [1, 0, 0, 0] keeps
+    feature 0 only."""
+    q = np.array([[[1, 0, 0, 0], [1, 0, 0, 0], [1, 0.5, -1, 0], [0, 0.5, -1, 0.5]]], np.float32)
+    k = np.array([[[[1, 1, 1, 1], [2, 2, 2, 2]], [[1, 2, 4, 8], [0.5, -1, 3, -2]]]], np.float32)
+    ug = np.array([[[0.75, 0.25, 0.9, 0.5]], [[0.25, 0.75, 0.9, 0.1]]], np.float32)
+    prob = _f32_problem(1, 4, 2, 4, 2)
+    assert O.bernoulli_coefs(np.array([0.5, 0.5, -1, 0.25], np.float32), ug[1], 1)[0].tolist() == [1, 0, -1, 1]
+    assert O.bernoulli_coefs(np.array([0.5, 0.5, -1, 0.25], np.float32), ug[0], 1)[0].tolist() == [0, 1, -1, 0]
+    for h in (2, 3):
+        x, nz = O.bernoulli_logits(prob, q, k, 1, True, ug, 0, h)
+        assert nz == 3 and x.tolist() == [5.0, -4.5], h
+    for h in (0, 1):
+        x, nz = O.bernoulli_logits(prob, q, k, 1, True, ug, 0, h)
+        assert nz == 1 and x.tolist() == [1.0, 2.0], h
+    assert O.bernoulli_features(prob, q, 1, True, ug).tolist() == [1, 3]
+
+
 @pytest.mark.parametrize("draws", [1, 2])
 def test_bernoulli_variance_closed_form(draws):
     """Var of the score estimate = scale^2 (a/draws)^2 sum_i K_i^2 draws p_i (1 - p_i)
