@@ -568,6 +568,54 @@ def test_prop_split_heads_match_one_workgroup_per_head(gpu, sampler, B):
     _say(f"split heads ({sampler}, {B} copies): indices and budgets equal, output max diff {err:.3g}")
 
 
+def _random_case(i):
+    """One seeded draw of a small problem mixing the axes the other tests
+    take one at a time: storage type, group size, KV heads, tile length,
+    batch, contiguous or paged, ragged (also empty) requests, planted keys or
+    flat attention, sample count and threshold generator."""
+    rng = np.random.default_rng([0xC0B0, i])
+    kv = ["bf16", "fp8", "f32"][int(rng.integers(3))]
+    T = int(rng.choice([64, 128, 256, 512, 1024]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([g for g in (1, 2, 4, 8) if g * Hkv <= 32]))
+    B = int(rng.integers(1, 5))
+    n = int(rng.integers(1, 6001))
+    paged = bool(rng.random() < 0.35)
+    hot, sinks = [(0, 0), (8, 0), (64, 4)][int(rng.integers(3))]
+    kw = dict(batch=B, num_q_heads=G * Hkv, num_kv_heads=Hkv, seq_len=n, tile_len=T,
+              q_dtype="f32" if kv == "f32" else "bf16", kv_dtype=kv)
+    if paged:
+        cfg = synth.small_config(5, min_seq_len=int(rng.integers(1, n + 1)), **kw)
+        lens = None
+    else:
+        cfg = synth.small_config(2, hot=hot, sinks=sinks, **kw)
+        lens = rng.integers(0, n + 1, size=B) if rng.random() < 0.5 else None
+    S = int(rng.choice([1, 3, 64, 128, 333, 1024, 4096]))
+    sampler = ["sys", "strat", "iid"][int(rng.integers(3))]
+    return cfg, lens, S, sampler, int(rng.integers(1 << 30))
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_combinations(gpu, case):
+    """prop (and, on equal-length contiguous requests, flash) and the exact
+    decode on a seeded random mix of shapes and options, each held to the
+    oracle bar."""
+    import parity
+    cfg, lens, S, sampler, seed = _random_case(case)
+    what = (f"case {case}: kv {cfg.kv_dtype}, T {cfg.tile_len}, Hq/Hkv {cfg.num_q_heads}/{cfg.num_kv_heads}, "
+            f"B {cfg.batch}, n {cfg.seq_len}, paged {cfg.page_size}, lens {None if lens is None else list(lens)}, "
+            f"hot {cfg.hot}+{cfg.sinks}, S {S}, {sampler}")
+    _say(what)
+    dev = _dev(cfg, seed, gpu, seq_lens=lens)
+    _say("  prop", parity.check_prop(dev, S, sampler=sampler))
+    _say("  exact", parity.check_exact(dev))
+    if not cfg.page_size and lens is None:
+        nt = -(-cfg.seq_len // cfg.tile_len)
+        Sf = int(np.random.default_rng(case).choice([1, 2, 4]))
+        Sf = min(Sf, cfg.tile_len)
+        _say("  flash", nt * Sf, parity.check_flash(dev, nt * Sf, sampler=sampler))
+
+
 # ------------------------------------------------- Bernoulli qK^T + prop
 @pytest.mark.parametrize("T", [64, 256, 1024])
 @pytest.mark.parametrize("draws,group_mean", [(1, 0), (4, 0), (4, 1), (16, 1)])
