@@ -638,6 +638,33 @@ def test_bernoulli_prop_groups(gpu, hq, hkv, T, group_mean):
     _say("bernoulli G", hq // hkv, "T", T, "mean", group_mean, rep)
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_bernoulli_random_combinations(gpu, case):
+    """Prop on Bernoulli scores over a seeded random mix: bf16 or e4m3 KV,
+    group size, KV heads, tile length, batch, ragged (also empty) requests,
+    planted keys or none, draws, per-head or mean group query, and S."""
+    import parity
+    rng = np.random.default_rng([0xBE70, case])
+    kv = ["bf16", "fp8"][int(rng.integers(2))]
+    T = int(rng.choice([64, 128, 256, 512, 1024]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([g for g in (1, 2, 4, 8) if g * Hkv <= 32]))
+    B = int(rng.integers(1, 4))
+    n = 4 * int(rng.integers(1, 1501))                 # the feature-major copy takes 4 keys per lane load
+    hot, sinks = [(0, 0), (8, 0), (64, 4)][int(rng.integers(3))]
+    lens = rng.integers(0, n + 1, size=B) if rng.random() < 0.5 else None
+    draws = int(rng.choice([1, 2, 4, 16]))
+    gm = int(rng.integers(2))
+    S = int(rng.choice([1, 3, 64, 128, 1024]))
+    cfg = synth.small_config(2, batch=B, num_q_heads=G * Hkv, num_kv_heads=Hkv, seq_len=n, tile_len=T,
+                             kv_dtype=kv, hot=hot, sinks=sinks)
+    _say(f"case {case}: kv {kv}, T {T}, Hq/Hkv {G * Hkv}/{Hkv}, B {B}, n {n}, "
+         f"lens {None if lens is None else [int(x) for x in lens]}, hot {hot}+{sinks}, draws {draws}, "
+         f"mean {gm}, S {S}")
+    dev = _dev(cfg, int(rng.integers(1 << 30)), gpu, seq_lens=lens)
+    _say("  bernoulli", parity.check_prop_bernoulli(dev, S, draws, gm))
+
+
 def test_bernoulli_prop_empty_ragged_and_tiny(gpu):
     """Requests of 0, 4, 300 and 2996 keys in a 3000-key cache, and a cache
     of 4 keys (one partial tile)."""
