@@ -597,9 +597,9 @@ def _random_case(i):
 
 @pytest.mark.parametrize("case", range(24))
 def test_random_combinations(gpu, case):
-    """prop (and, on equal-length contiguous requests, flash) and the exact
-    decode on a seeded random mix of shapes and options, each held to the
-    oracle bar."""
+    """prop (also in its single launch, with systematic thresholds; and, on
+    equal-length contiguous requests, flash) and the exact decode on a
+    seeded random mix of shapes and options, each held to the oracle bar."""
     import parity
     cfg, lens, S, sampler, seed = _random_case(case)
     what = (f"case {case}: kv {cfg.kv_dtype}, T {cfg.tile_len}, Hq/Hkv {cfg.num_q_heads}/{cfg.num_kv_heads}, "
@@ -608,6 +608,8 @@ def test_random_combinations(gpu, case):
     _say(what)
     dev = _dev(cfg, seed, gpu, seq_lens=lens)
     _say("  prop", parity.check_prop(dev, S, sampler=sampler))
+    if sampler == "sys":
+        _say("  single-launch prop", parity.check_prop(dev, S, fused=True))
     _say("  exact", parity.check_exact(dev))
     if not cfg.page_size and lens is None:
         nt = -(-cfg.seq_len // cfg.tile_len)
