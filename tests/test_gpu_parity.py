@@ -270,6 +270,34 @@ def test_prop_tiny_sequences(gpu):
         _say("n", n, rep)
 
 
+def test_output_overlapping_the_query_is_rejected(gpu):
+    """Prop clears output rows while other workgroups still read the query,
+    so an output that shares memory with q (or with the offsets) is refused
+    on the host before anything is launched, and the memory keeps its
+    contents."""
+    import torch
+    import stochastic_sparse_attention_amd as sa
+    from stochastic_sparse_attention_amd._lib import SantaError, SANTA_ERR_INVALID
+    cfg = synth.small_config(2, batch=1, seq_len=1024)
+    dev = _dev(cfg, 3, gpu)
+    BH, d, S = cfg.batch * cfg.num_q_heads, cfg.head_dim, cfg.S
+    buf = torch.zeros(BH * d, dtype=torch.float32, device=gpu)
+    q = buf.view(torch.bfloat16)[:BH * d].view(cfg.batch, cfg.num_q_heads, d)
+    q.copy_(dev.q.view(cfg.batch, cfg.num_q_heads, d))
+    before = buf.clone()
+    for call in (lambda: sa.santa_decode_prop(dev.problem, q, dev.k, dev.v, S, dev.u(S), buf.view(BH, d)),
+                 lambda: sa.exact_decode_ref(dev.problem, q, dev.k, dev.v, buf.view(BH, d))):
+        with pytest.raises(SantaError) as e:
+            call()
+        assert e.value.status == SANTA_ERR_INVALID
+    u = torch.zeros(BH * d, dtype=torch.float32, device=gpu)
+    with pytest.raises(SantaError):
+        sa.santa_decode_prop(dev.problem, dev.q, dev.k, dev.v, S, u[:BH], u.view(BH, d))
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before)
+    _say("outputs overlapping q or u are refused")
+
+
 def test_prop_one_hot_gives_exact_row(gpu):
     """A logit gap of hundreds makes A one-hot: the output is exactly that V row."""
     import parity
