@@ -298,6 +298,44 @@ def test_output_overlapping_the_query_is_rejected(gpu):
     _say("outputs overlapping q or u are refused")
 
 
+@pytest.mark.parametrize("cid", [2, 3, 8])
+def test_optional_outputs_do_not_change_the_estimate(gpu, cid):
+    """The benchmark times the calls without the optional index list and
+    budgets (and, on Bernoulli scores, read counts).  At the full workload
+    sizes those calls give bitwise the estimate of the calls that write them,
+    which the full-size parity tests hold to the oracle: prop with each
+    generator, flash where the workload has a flash budget, and prop on
+    Bernoulli scores with the mean group query."""
+    import torch
+    import parity
+    import stochastic_sparse_attention_amd as sa
+    cfg = synth.CONFIGS[cid]
+    _say(f"config {cid}: optional outputs off vs on")
+    dev = _dev(cfg, 7, gpu)
+    BH, d, S = cfg.batch * cfg.num_q_heads, cfg.head_dim, cfg.S
+    out = torch.empty((BH, d), dtype=torch.float32, device=gpu)
+    for sampler in ("sys", "strat", "iid"):
+        ref, _, _ = parity.run_prop(dev, S, sampler=sampler)
+        if sampler == "sys":
+            sa.santa_decode_prop(dev.problem, dev.q, dev.k, dev.v, S, dev.u(S), out)
+        else:
+            sa.santa_decode_prop_sampler(dev.problem, dev.q, dev.k, dev.v, S, sampler, dev.uniforms(S), out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32)), sampler
+    if cfg.S_flash:
+        ref, _ = parity.run_flash(dev, cfg.S_flash)
+        sa.santa_decode_flash(dev.problem, dev.q, dev.k, dev.v, cfg.S_flash, dev.u(cfg.S_flash), out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    kf = dev.k_features()
+    ref, _, _, _ = parity.run_prop_bernoulli(dev, S, 4, 1, kf)
+    sa.santa_decode_prop_bernoulli(dev.problem, dev.q, kf, dev.v, S, dev.u(S), 4, 1,
+                                   dev.bernoulli_uniforms(4, 1), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    _say(f"config {cid}: bitwise equal with and without the optional outputs")
+
+
 def test_prop_one_hot_gives_exact_row(gpu):
     """A logit gap of hundreds makes A one-hot: the output is exactly that V row."""
     import parity
